@@ -1,0 +1,247 @@
+"""ctypes binding of the C oracle (oracle.c) for numpy arrays on the host.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the package smoke check and the benchmark's
+CPU-baseline leg, never by the product path.  Every function is a thin marshalling wrapper: the
+arithmetic, and the page citation for it, live in oracle.c.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+E4M3, E5M2 = 0, 1
+IN_F32, IN_BF16 = 0, 1
+TENSOR, BLOCK, MX, MOSS = 0, 1, 2, 3
+FP8_MAX = {E4M3: 448.0, E5M2: 57344.0}
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with plain gcc (no fast-math) into liboracle.so next to it."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-std=c11", "-fPIC", "-shared",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I64, I, F, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_double
+        sig = {
+            "orc_fp8_max": (D, [I]),
+            "orc_fp8_decode": (D, [I, I]),
+            "orc_fp8_encode": (ctypes.c_uint8, [F, I]),
+            "orc_fp8_encode_array": (None, [P, I64, I, P]),
+            "orc_fp8_decode_array": (None, [P, I64, I, P]),
+            "orc_amax": (F, [P, I, I64, I64, I64]),
+            "orc_compute_scale": (F, [F, I, F]),
+            "orc_quantize_value": (ctypes.c_uint8, [F, F, I]),
+            "orc_quantize_tensor": (None, [P, I, I64, I64, I64, I, F, I, P, I64]),
+            "orc_quantize_block": (None, [P, I, I64, I64, I64, I, I64, I64, I, P, I64, P]),
+            "orc_quantize_mx": (None, [P, I, I64, I64, I64, I, I, P, I64, P]),
+            "orc_quantize_moss": (None, [P, I, I64, I64, I64, I, I, P, I64, P, P]),
+            "orc_history_roll_insert": (None, [P, I64, F]),
+            "orc_history_max": (F, [P, I64]),
+            "orc_delayed_step": (None, [P, I, I64, I64, I64, I, I, P, P, I64, P, I64, P]),
+            "orc_dequantize": (None, [I, P, I, I64, I64, I64, P, I64, I64, P, P]),
+            "orc_gemm_ref": (None, [P, P, I64, I64, I64, P, I64, P, P]),
+            "orc_snr_db": (D, [P, P, I64]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _input(x: np.ndarray):
+    """(array, in_kind): fp32 arrays as-is, bf16 given as uint16 bit patterns."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float32:
+        return x, IN_F32
+    if x.dtype == np.uint16:
+        return x, IN_BF16
+    raise TypeError("oracle inputs are float32 or bf16 bit patterns (uint16), got %s" % x.dtype)
+
+
+# ------------------------------------------------------------------ codec
+def fp8_max(fmt: int) -> float:
+    return lib().orc_fp8_max(fmt)
+
+
+def decode(code: int, fmt: int) -> float:
+    return lib().orc_fp8_decode(int(code), fmt)
+
+
+def encode(v: float, fmt: int) -> int:
+    return int(lib().orc_fp8_encode(float(np.float32(v)), fmt))
+
+
+def encode_array(v: np.ndarray, fmt: int) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, np.uint8)
+    lib().orc_fp8_encode_array(_p(v), v.size, fmt, _p(out))
+    return out
+
+
+def decode_array(q: np.ndarray, fmt: int) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    out = np.empty(q.shape, np.float64)
+    lib().orc_fp8_decode_array(_p(q), q.size, fmt, _p(out))
+    return out
+
+
+# ------------------------------------------------------------------ amax / scales
+def amax(x: np.ndarray) -> np.float32:
+    x, kind = _input(x)
+    r, c = x.shape
+    return np.float32(lib().orc_amax(_p(x), kind, r, c, c))
+
+
+def compute_scale(a: float, fmt: int, fallback: float) -> np.float32:
+    return np.float32(lib().orc_compute_scale(float(a), fmt, float(fallback)))
+
+
+def quantize_value(x: float, s: float, fmt: int) -> int:
+    return int(lib().orc_quantize_value(float(x), float(s), fmt))
+
+
+# ------------------------------------------------------------------ schemes
+def _out_shape(x, transpose):
+    r, c = x.shape
+    return (c, r) if transpose else (r, c)
+
+
+def quantize_tensor(x: np.ndarray, fmt: int, scale: float, transpose: bool = False) -> np.ndarray:
+    x, kind = _input(x)
+    R, C = _out_shape(x, transpose)
+    q = np.empty((R, C), np.uint8)
+    lib().orc_quantize_tensor(_p(x), kind, x.shape[0], x.shape[1], x.shape[1], fmt,
+                              float(scale), int(transpose), _p(q), C)
+    return q
+
+
+def quantize_tensor_current(x: np.ndarray, fmt: int, transpose: bool = False):
+    """Current per-tensor scaling: scale = amax/MAX (fallback 1), then quantize."""
+    s = compute_scale(amax(x), fmt, 1.0)
+    return quantize_tensor(x, fmt, s, transpose), s
+
+
+def quantize_block(x: np.ndarray, fmt: int, br: int, bc: int, transpose: bool = False):
+    x, kind = _input(x)
+    R, C = _out_shape(x, transpose)
+    q = np.empty((R, C), np.uint8)
+    s = np.empty(((R + br - 1) // br, (C + bc - 1) // bc), np.float32)
+    lib().orc_quantize_block(_p(x), kind, x.shape[0], x.shape[1], x.shape[1], fmt, br, bc,
+                             int(transpose), _p(q), C, _p(s))
+    return q, s
+
+
+def quantize_mx(x: np.ndarray, fmt: int, transpose: bool = False):
+    x, kind = _input(x)
+    R, C = _out_shape(x, transpose)
+    q = np.empty((R, C), np.uint8)
+    e = np.empty((R, (C + 31) // 32), np.uint8)
+    lib().orc_quantize_mx(_p(x), kind, x.shape[0], x.shape[1], x.shape[1], fmt, int(transpose),
+                          _p(q), C, _p(e))
+    return q, e
+
+
+def quantize_moss(x: np.ndarray, fmt: int, transpose: bool = False):
+    x, kind = _input(x)
+    R, C = _out_shape(x, transpose)
+    q = np.empty((R, C), np.uint8)
+    e = np.empty((R, (C + 31) // 32), np.uint8)
+    S = np.zeros(1, np.float32)
+    lib().orc_quantize_moss(_p(x), kind, x.shape[0], x.shape[1], x.shape[1], fmt, int(transpose),
+                            _p(q), C, _p(e), _p(S))
+    return q, e, S[0]
+
+
+# ------------------------------------------------------------------ delayed scaling
+def history_roll_insert(hist: np.ndarray, a: float) -> None:
+    assert hist.dtype == np.float32 and hist.flags.c_contiguous
+    lib().orc_history_roll_insert(_p(hist), hist.size, float(a))
+
+
+def history_max(hist: np.ndarray) -> np.float32:
+    hist = np.ascontiguousarray(hist, np.float32)
+    return np.float32(lib().orc_history_max(_p(hist), hist.size))
+
+
+def delayed_step(x: np.ndarray, fmt: int, scale: np.ndarray, hist: np.ndarray, transpose: bool = False):
+    """Flax in-step order: scale from max(history) (previous kept on zero/non-finite), quantize,
+    then roll-insert amax(x).  `scale` (shape (1,) fp32) and `hist` are updated in place."""
+    x, kind = _input(x)
+    assert scale.dtype == np.float32 and hist.dtype == np.float32
+    R, C = _out_shape(x, transpose)
+    q = np.empty((R, C), np.uint8)
+    a = np.zeros(1, np.float32)
+    lib().orc_delayed_step(_p(x), kind, x.shape[0], x.shape[1], x.shape[1], fmt, int(transpose),
+                           _p(scale), _p(hist), hist.size, _p(q), C, _p(a))
+    return q, a[0]
+
+
+# ------------------------------------------------------------------ dequant / GEMM / SNR
+def dequantize(mode: int, q: np.ndarray, fmt: int, scales=None, global_scale=None,
+               block=(1, 128)) -> np.ndarray:
+    """fp64 dequantized operand (rows x K): q times its scale(s), exact."""
+    q = np.ascontiguousarray(q, np.uint8)
+    rows, K = q.shape
+    out = np.empty((rows, K), np.float64)
+    g = np.array([1.0 if global_scale is None else global_scale], np.float32)
+    if mode == BLOCK:
+        sc = np.ascontiguousarray(scales, np.float32)
+    elif mode in (MX, MOSS):
+        sc = np.ascontiguousarray(scales, np.uint8)
+    else:
+        sc = np.zeros(1, np.float32)
+    lib().orc_dequantize(mode, _p(q), fmt, rows, K, K, _p(sc), block[0], block[1], _p(g), _p(out))
+    return out
+
+
+def gemm_ref(A: np.ndarray, B: np.ndarray, pairs: np.ndarray | None = None):
+    """fp64 C = A @ B.T and D = |A| @ |B|.T over dequantized operands (rows x K each).
+    With `pairs` (n x 2 int64 of (m, n)), only those entries are returned (1-D)."""
+    A = np.ascontiguousarray(A, np.float64)
+    B = np.ascontiguousarray(B, np.float64)
+    M, K = A.shape
+    N, K2 = B.shape
+    assert K == K2
+    if pairs is None:
+        C = np.empty((M, N), np.float64)
+        D = np.empty((M, N), np.float64)
+        lib().orc_gemm_ref(_p(A), _p(B), M, N, K, None, 0, _p(C), _p(D))
+        return C, D
+    pairs = np.ascontiguousarray(pairs, np.int64)
+    n = pairs.shape[0]
+    C = np.empty(n, np.float64)
+    D = np.empty(n, np.float64)
+    lib().orc_gemm_ref(_p(A), _p(B), M, N, K, _p(pairs), n, _p(C), _p(D))
+    return C, D
+
+
+def snr_db(x: np.ndarray, xhat: np.ndarray) -> float:
+    x = np.ascontiguousarray(x, np.float32)
+    xhat = np.ascontiguousarray(xhat, np.float64)
+    assert x.size == xhat.size
+    return float(lib().orc_snr_db(_p(x), _p(xhat), x.size))

@@ -1,0 +1,124 @@
+"""Pins for the oracle's dequantization, fp64 GEMM reference and SNR: exact rational brute force on
+tiny shapes, reductions to plain matmul, numpy's float64 matmul as an independent library
+routine, and hand-computed SNR values (the MOSS page: +3 dB is half the noise power)."""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from fp8_scaled_quantization_amd import workloads
+from tests import brute
+
+E4M3, E5M2 = 0, 1
+TENSOR, BLOCK, MX, MOSS = 0, 1, 2, 3
+
+
+def test_gemm_ref_exact_rational_tiny(orc):
+    rng = np.random.default_rng(7)
+    M, N, K = 3, 4, 64
+    qa = rng.integers(0, 0x7F, (M, K)).astype(np.uint8)
+    qb = rng.integers(0x80, 0xFF, (N, K)).astype(np.uint8)
+    sa, sb = np.float32(0.0371), np.float32(1.7e-3)
+    A = orc.dequantize(TENSOR, qa, E4M3, None, sa)
+    B = orc.dequantize(TENSOR, qb, E4M3, None, sb)
+    C, D = orc.gemm_ref(A, B)
+    for m in range(M):
+        for n in range(N):
+            exact = sum(brute.fp8_value(int(qa[m, k]), E4M3) * brute.fp8_value(int(qb[n, k]), E4M3)
+                        for k in range(K)) * Fraction(float(sa)) * Fraction(float(sb))
+            absum = sum(abs(brute.fp8_value(int(qa[m, k]), E4M3) * brute.fp8_value(int(qb[n, k]), E4M3))
+                        for k in range(K)) * Fraction(float(sa)) * Fraction(float(sb))
+            assert abs(Fraction(C[m, n]) - exact) <= Fraction(1, 10 ** 14) * absum
+            assert abs(Fraction(D[m, n]) - absum) <= Fraction(1, 10 ** 14) * absum
+
+
+def test_gemm_ref_vs_numpy_matmul_and_sampling(orc):
+    rng = np.random.default_rng(8)
+    A = rng.standard_normal((40, 300))
+    B = rng.standard_normal((24, 300))
+    C, D = orc.gemm_ref(A, B)
+    assert np.allclose(C, A @ B.T, rtol=0, atol=1e-12 * np.abs(A).max() * np.abs(B).max() * 300)
+    assert np.allclose(D, np.abs(A) @ np.abs(B).T, rtol=1e-13)
+    pairs = np.array([[0, 0], [39, 23], [17, 5]], np.int64)
+    Cs, Ds = orc.gemm_ref(A, B, pairs)
+    assert np.array_equal(Cs, C[pairs[:, 0], pairs[:, 1]]) and np.array_equal(Ds, D[pairs[:, 0], pairs[:, 1]])
+
+
+def test_lossless_operands_reduce_to_plain_matmul(orc):
+    # integer-valued operands on the E4M3 grid, quantized with scale 1: the reference is the
+    # exact integer product
+    rng = np.random.default_rng(9)
+    a = rng.integers(-16, 17, (8, 96)).astype(np.float32)
+    b = rng.integers(-16, 17, (12, 96)).astype(np.float32)
+    qa = orc.quantize_tensor(a, E4M3, 1.0)
+    qb = orc.quantize_tensor(b, E4M3, 1.0)
+    C, _ = orc.gemm_ref(orc.dequantize(TENSOR, qa, E4M3, None, 1.0), orc.dequantize(TENSOR, qb, E4M3, None, 1.0))
+    assert np.array_equal(C, a.astype(np.float64) @ b.astype(np.float64).T)
+
+
+def test_block_dequant_with_equal_scales_is_per_tensor(orc):
+    rng = np.random.default_rng(10)
+    q = rng.integers(0, 0x7E, (256, 256)).astype(np.uint8)
+    s = np.full((2, 2), 0.25, np.float32)
+    assert np.array_equal(orc.dequantize(BLOCK, q, E4M3, s, None, block=(128, 128)),
+                          orc.dequantize(TENSOR, q, E4M3, None, 0.25))
+    s1 = np.full((256, 2), 0.25, np.float32)
+    assert np.array_equal(orc.dequantize(BLOCK, q, E4M3, s1, None, block=(1, 128)),
+                          orc.dequantize(TENSOR, q, E4M3, None, 0.25))
+
+
+def test_block_dequant_layout(orc):
+    q = np.full((256, 256), 0x38, np.uint8)          # all ones
+    s = np.array([[1.0, 2.0], [3.0, 4.0]], np.float32)
+    d = orc.dequantize(BLOCK, q, E4M3, s, None, block=(128, 128))
+    assert d[0, 0] == 1.0 and d[0, 255] == 2.0 and d[255, 0] == 3.0 and d[200, 200] == 4.0
+
+
+def test_mx_and_moss_dequant_powers_of_two(orc):
+    q = np.full((2, 64), 0x38, np.uint8)
+    e = np.array([[127, 130], [120, 127]], np.uint8)
+    d = orc.dequantize(MX, q, E4M3, e)
+    assert d[0, 0] == 1.0 and d[0, 40] == 8.0 and d[1, 0] == 2.0 ** -7
+    d2 = orc.dequantize(MOSS, q, E4M3, e, np.float32(0.5))
+    assert np.array_equal(d2, d * 0.5)
+    # all exponents zero: MX is plain unscaled FP8
+    e0 = np.full((2, 2), 127, np.uint8)
+    assert np.array_equal(orc.dequantize(MX, q, E4M3, e0), orc.decode_array(q, E4M3))
+
+
+def test_quantize_dequantize_roundtrip_error(orc):
+    X, W, dY = workloads.moss_inputs(tokens=64, d_in=256, d_out=128)
+    x = workloads.bf16_bits_to_f32(X).astype(np.float64)
+    q, e, S = orc.quantize_moss(X, E4M3)
+    xh = orc.dequantize(MOSS, q, E4M3, e, S)
+    loc = np.repeat(np.ldexp(1.0, e.astype(np.int64) - 127), 32, axis=1) * float(S)
+    # E4M3 normal range: relative error at most 2^-4; subnormal range: absolute 2^-10 * scale
+    assert np.all(np.abs(x - xh) <= np.maximum(2.0 ** -4 * np.abs(x), 2.0 ** -10 * loc) * (1 + 1e-6))
+
+
+def test_snr_hand_values(orc):
+    x = np.array([3.0, 4.0], np.float32)
+    assert orc.snr_db(x, np.array([3.0, 4.1])) == pytest.approx(10 * math.log10(25 / 0.01), rel=1e-9)
+    assert orc.snr_db(x, x.astype(np.float64)) == math.inf
+    rng = np.random.default_rng(12)
+    y = rng.standard_normal(1000).astype(np.float32)
+    noise = rng.standard_normal(1000) * 0.01
+    s1 = orc.snr_db(y, y.astype(np.float64) + noise)
+    s2 = orc.snr_db(y, y.astype(np.float64) + noise / math.sqrt(2))
+    assert s2 - s1 == pytest.approx(10 * math.log10(2), abs=1e-9)      # half the noise power: +3.01 dB
+
+
+def test_snr_ordering_on_workload_like_data(orc):
+    """MOSS >= per-tensor is a theorem (same global factor, finer power-of-two grid); per-group
+    1x128 >= per-tensor holds on these workloads.  MOSS vs per-group is only reported."""
+    X, W, dY = workloads.moss_inputs(tokens=256, d_in=512, d_out=256)
+    for src, fmt in ((X, E4M3), (W, E4M3), (dY, E5M2)):
+        x = workloads.bf16_bits_to_f32(src)
+        qt, st = orc.quantize_tensor_current(src, fmt)
+        qg, sg = orc.quantize_block(src, fmt, 1, 128)
+        qm, em, S = orc.quantize_moss(src, fmt)
+        snr_t = orc.snr_db(x, orc.dequantize(TENSOR, qt, fmt, None, st))
+        snr_g = orc.snr_db(x, orc.dequantize(BLOCK, qg, fmt, sg, None, block=(1, 128)))
+        snr_m = orc.snr_db(x, orc.dequantize(MOSS, qm, fmt, em, S))
+        assert snr_m >= snr_t and snr_g >= snr_t
