@@ -1,0 +1,196 @@
+// C ABI entry points (include/fp8q.h): argument validation, error reporting and dispatch to the
+// kernel launchers.  No allocation, no synchronization: all work goes on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/fp8q.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int check_launch(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(FP8Q_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return FP8Q_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Per-device result of the architecture check (up to 64 devices).
+int g_arch_ok[64];   // 0 unknown, 1 gfx950, -1 other
+
+int check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(FP8Q_ERR_NO_DEVICE, "no HIP device is current");
+    if (dev < 0 || dev >= 64) return fail(FP8Q_ERR_NO_DEVICE, "device index %d out of range", dev);
+    if (g_arch_ok[dev] == 0) {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, dev) != hipSuccess) return fail(FP8Q_ERR_NO_DEVICE, "cannot query device %d", dev);
+        g_arch_ok[dev] = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    }
+    if (g_arch_ok[dev] != 1) return fail(FP8Q_ERR_NO_DEVICE, "device %d is not gfx950 (MI355X)", dev);
+    return FP8Q_OK;
+}
+
+bool valid_fmt(int f) { return f == FP8Q_E4M3 || f == FP8Q_E5M2; }
+bool valid_in(int d) { return d == FP8Q_IN_F32 || d == FP8Q_IN_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+int fp8q_init(void) {
+    g_err[0] = 0;
+    return check_device();
+}
+
+const char* fp8q_last_error(void) { return g_err; }
+
+int fp8_amax(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld, float* amax_out, void* stream) {
+    g_err[0] = 0;
+    if (!valid_in(in_dtype)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_amax: in_dtype %d is not FP8Q_IN_F32/BF16", in_dtype);
+    if (rows < 0 || cols < 0 || ld < cols) return fail(FP8Q_ERR_INVALID_ARG, "fp8_amax: bad shape rows=%lld cols=%lld ld=%lld",
+                                                      (long long)rows, (long long)cols, (long long)ld);
+    if (!amax_out || (!x && rows * cols > 0)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_amax: NULL pointer");
+    if (cols % 8 || ld % 8 || !aligned16(x)) return fail(FP8Q_ERR_UNSUPPORTED, "fp8_amax: cols and ld must be multiples of 8 and x 16-byte aligned");
+    int rc = check_device();
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    fp8q::launch_amax(x, in_dtype == FP8Q_IN_BF16, rows, cols, ld, amax_out, st);
+    return check_launch("fp8_amax");
+}
+
+int fp8_quantize(int mode, int fmt, const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld,
+                 int block_r, int block_c, int transpose_out, uint8_t* q, int64_t ldq, void* scales,
+                 float* tensor_scale, int scale_is_input, float* amax_out, void* stream) {
+    g_err[0] = 0;
+    if (mode < FP8Q_TENSOR || mode > FP8Q_MOSS) return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: unknown mode %d", mode);
+    if (!valid_fmt(fmt)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: fmt %d is not FP8Q_E4M3/E5M2", fmt);
+    if (!valid_in(in_dtype)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: in_dtype %d is not FP8Q_IN_F32/BF16", in_dtype);
+    if (transpose_out != 0 && transpose_out != 1) return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: transpose_out must be 0 or 1");
+    if (rows < 0 || cols < 0 || ld < cols) return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: bad shape rows=%lld cols=%lld ld=%lld",
+                                                      (long long)rows, (long long)cols, (long long)ld);
+    const int64_t R = transpose_out ? cols : rows, K = transpose_out ? rows : cols;
+    if (ldq < K) return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: ldq=%lld is smaller than the output row length %lld",
+                             (long long)ldq, (long long)K);
+    const bool empty = rows * cols == 0;
+    if (!empty && (!x || !q)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: NULL x or q");
+    if (mode == FP8Q_BLOCK && (block_r <= 0 || block_c <= 0))
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: block size (%d, %d) must be two positive integers", block_r, block_c);
+    if (mode != FP8Q_TENSOR && !scales && !empty) return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: NULL scales");
+    const bool needs_amax = (mode == FP8Q_TENSOR || mode == FP8Q_MOSS) && !scale_is_input;
+    if ((mode == FP8Q_TENSOR || mode == FP8Q_MOSS) && !tensor_scale)
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: tensor_scale is required for TENSOR and MOSS");
+    if (needs_amax && !amax_out)
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: amax_out is required when the scale is derived (scale_is_input=0)");
+    if (cols % 8 || ld % 8 || !aligned16(x))
+        return fail(FP8Q_ERR_UNSUPPORTED, "fp8_quantize: needs cols %% 8 == 0, ld %% 8 == 0 and a 16-byte aligned x");
+    (void)R;
+    int rc = check_device();
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool bf16 = in_dtype == FP8Q_IN_BF16;
+
+    fp8q::CastArgs a{};
+    a.mode = mode;
+    a.fmt = fmt;
+    a.x = x;
+    a.bf16 = bf16;
+    a.rows = rows;
+    a.cols = cols;
+    a.ld = ld;
+    a.transpose = transpose_out != 0;
+    a.q = q;
+    a.ldq = ldq;
+    a.scales = scales;
+    a.block_r = block_r;
+    a.block_c = block_c;
+    a.vec_out = ldq % 16 == 0 && aligned16(q);
+    if (mode == FP8Q_TENSOR || mode == FP8Q_MOSS) {
+        if (needs_amax) {
+            fp8q::launch_amax(x, bf16, rows, cols, ld, amax_out, st);
+            a.amax_in = amax_out;
+            a.scale_out = tensor_scale;
+        } else {
+            a.scale_in = tensor_scale;
+            if (mode == FP8Q_TENSOR && amax_out) {
+                fp8q::launch_zero_u32(amax_out, st);
+                a.amax_out = amax_out;
+            }
+        }
+    }
+    if (needs_amax && empty) {
+        // amax of an empty tensor is 0: the scale falls back to 1 (no cast kernel runs)
+        fp8q::launch_fill_f32(tensor_scale, 1.0f, st);
+    }
+    fp8q::launch_cast(a, st);
+    return check_launch("fp8_quantize");
+}
+
+int fp8_history_update(float* history, int64_t len, const float* amax_new, float* scale_inout, int fmt, void* stream) {
+    g_err[0] = 0;
+    if (!valid_fmt(fmt)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_history_update: fmt %d is not FP8Q_E4M3/E5M2", fmt);
+    if (len < 1 || len > 4096) return fail(FP8Q_ERR_INVALID_ARG, "fp8_history_update: len=%lld outside [1, 4096]", (long long)len);
+    if (!history || !amax_new || !scale_inout) return fail(FP8Q_ERR_INVALID_ARG, "fp8_history_update: NULL pointer");
+    int rc = check_device();
+    if (rc) return rc;
+    fp8q::launch_history(history, (int)len, amax_new, scale_inout, fmt, static_cast<hipStream_t>(stream));
+    return check_launch("fp8_history_update");
+}
+
+int fp8_scaled_gemm(int mode, const uint8_t* A, int afmt, const void* Ascale, const uint8_t* B, int bfmt,
+                    const void* Bscale, const float* Aglobal, const float* Bglobal, int64_t M, int64_t N, int64_t K,
+                    int64_t lda, int64_t ldb, void* C, int out_dtype, int64_t ldc, void* stream) {
+    g_err[0] = 0;
+    if (mode < FP8Q_TENSOR || mode > FP8Q_MOSS) return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: unknown mode %d", mode);
+    if (!valid_fmt(afmt) || !valid_fmt(bfmt)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: bad operand format");
+    if (out_dtype != FP8Q_OUT_F32 && out_dtype != FP8Q_OUT_BF16)
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: out_dtype %d is not FP8Q_OUT_F32/BF16 (it is required)", out_dtype);
+    if (M < 0 || N < 0 || K < 0 || lda < K || ldb < K || ldc < N)
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: bad shape M=%lld N=%lld K=%lld lda=%lld ldb=%lld ldc=%lld",
+                    (long long)M, (long long)N, (long long)K, (long long)lda, (long long)ldb, (long long)ldc);
+    if (M * N > 0 && !C) return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: NULL C");
+    if (M * N * K > 0 && (!A || !B)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: NULL A or B");
+    if ((mode == FP8Q_TENSOR || mode == FP8Q_MOSS) && (!Aglobal || !Bglobal))
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: Aglobal and Bglobal are required for TENSOR and MOSS");
+    if (mode != FP8Q_TENSOR && K > 0 && M * N > 0 && (!Ascale || !Bscale))
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: Ascale and Bscale are required for BLOCK, MX and MOSS");
+    if (K > 0 && (K % 16 || lda % 16 || ldb % 16 || !aligned16(A) || !aligned16(B)))
+        return fail(FP8Q_ERR_UNSUPPORTED, "fp8_scaled_gemm: needs K, lda, ldb multiples of 16 and 16-byte aligned A, B");
+    int rc = check_device();
+    if (rc) return rc;
+    fp8q::GemmArgs g{};
+    g.mode = mode;
+    g.afmt = afmt;
+    g.bfmt = bfmt;
+    g.A = A;
+    g.B = B;
+    g.Ascale = Ascale;
+    g.Bscale = Bscale;
+    g.Aglobal = Aglobal;
+    g.Bglobal = Bglobal;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.lda = lda;
+    g.ldb = ldb;
+    g.C = C;
+    g.out_bf16 = out_dtype == FP8Q_OUT_BF16;
+    g.ldc = ldc;
+    fp8q::launch_gemm(g, static_cast<hipStream_t>(stream));
+    return check_launch("fp8_scaled_gemm");
+}
+
+}  // extern "C"

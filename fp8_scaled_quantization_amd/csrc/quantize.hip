@@ -1,0 +1,395 @@
+// FP8 cast kernels for the five scaling schemes.
+//
+// Every element is RNE8(clip(fl(x / scale))) (page "Flax FP8 量化实战指南 ...", sections 1 and 2.2),
+// with the scale chosen per scheme:
+//   TENSOR  one fp32 scale: current (amax/MAX of the whole tensor) or supplied (delayed / static);
+//   BLOCK   one fp32 scale per 1x128 row group or 128x128 block (page "Transformers 中的细粒度 FP8
+//           量化配置 ...", section 一);
+//   MX      a power of two per 32 consecutive K values, chosen so that nothing clips (page "MOSS:
+//           高效、精确的 FP8 LLM 训练 ...", section 1); the element is x * 2^-e, exact scaling;
+//   MOSS    fp32 global S times a per-32 power-of-two local factor in (0, 1] (same page, section 4);
+//           the element is fl(x / S) * 2^-e_i.
+//
+// Work layout.  A "lane chunk" is 32 consecutive values along the output's K axis, owned by one
+// lane: an MX/MOSS group is exactly one lane (no cross-lane reduction) and a 1x128 group is four
+// adjacent lanes (two xor-shuffles).  The division by a scale uses y = RN(1/s) and one Markstein
+// correction, which equals IEEE division whenever the guards in common.cuh hold (exhaustively
+// checked over all dividend significands for thousands of divisors); chunks outside the guards,
+// and lanes holding NaN, use IEEE division and the NaN byte fix-up instead.
+#include "common.cuh"
+#include "kernels.h"
+
+namespace fp8q {
+
+// ------------------------------------------------------------------ per-chunk work
+struct ChunkStats {
+    uint32_t mx;      // max |x| bits
+    uint32_t mn;      // min (|x| bits - 1), zero wraps to 0xffffffff
+};
+
+__device__ __forceinline__ ChunkStats chunk_stats(const float* v) {
+    ChunkStats s{0u, 0xFFFFFFFFu};
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        uint32_t b = absbits(v[j]);
+        s.mx = max(s.mx, b);
+        s.mn = min(s.mn, b - 1u);
+    }
+    return s;
+}
+
+// out[i] packs codes of v[4i .. 4i+3]: element = clip(fl(v/s) * 2^shift).
+template <int FMT, bool SHIFT>
+__device__ __forceinline__ void cast32_div(const float* v, float s, float y, int shift, bool fast, uint32_t* out) {
+    if (fast) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float c[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float q = div_fast(v[4 * i + k], s, y);
+                if (SHIFT) q = __builtin_amdgcn_ldexpf(q, shift);
+                c[k] = clip<FMT>(q);
+            }
+            out[i] = cvt4<FMT>(c[0], c[1], c[2], c[3]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float q = v[4 * i + k] / s;
+                if (SHIFT) q = __builtin_amdgcn_ldexpf(q, shift);
+                w |= code_slow<FMT>(q) << (8 * k);
+            }
+            out[i] = w;
+        }
+    }
+}
+
+// MX element: clip(x * 2^shift), exact scaling; only NaN needs the slow path.
+template <int FMT>
+__device__ __forceinline__ void cast32_mx(const float* v, int shift, bool has_nan, uint32_t* out) {
+    if (!has_nan) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float c[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) c[k] = clip<FMT>(__builtin_amdgcn_ldexpf(v[4 * i + k], shift));
+            out[i] = cvt4<FMT>(c[0], c[1], c[2], c[3]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w |= code_slow<FMT>(__builtin_amdgcn_ldexpf(v[4 * i + k], shift)) << (8 * k);
+            out[i] = w;
+        }
+    }
+}
+
+// Tensor-uniform divisor state (TENSOR and MOSS).
+struct UniformScale {
+    float s, y;
+    bool ok;
+};
+
+template <int FMT, int MODE, bool DERIVE>
+__device__ __forceinline__ UniformScale uniform_scale(const CastArgs& a) {
+    UniformScale u{1.0f, 1.0f, true};
+    if (MODE == kModeTensor || MODE == kModeMoss) {
+        float s = DERIVE ? scale_from_amax<FMT>(*a.amax_in, 1.0f) : *a.scale_in;
+        u.s = s;
+        u.y = recip_rn(s);
+        u.ok = divisor_ok(s);
+        if (DERIVE && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.scale_out = s;
+    }
+    return u;
+}
+
+// Process one lane chunk v[32] (all 64 lanes of the wave call this together: BLOCK uses shuffles).
+// Returns the per-lane scale value to store (BLOCK: fp32 bits; MX/MOSS: E8M0 byte) in `sc`.
+template <int FMT, int MODE>
+__device__ __forceinline__ void process_chunk(const float* v, const UniformScale& u, uint32_t* out,
+                                              uint32_t& sc, uint32_t& chunk_max) {
+    ChunkStats st = chunk_stats(v);
+    chunk_max = st.mx;
+    if (MODE == kModeTensor) {
+        cast32_div<FMT, false>(v, u.s, u.y, 0, u.ok && dividends_ok(st.mx, st.mn), out);
+    } else if (MODE == kModeBlock) {
+        uint32_t gmx = group_max_u32<4>(st.mx);
+        float s = scale_from_amax<FMT>(__uint_as_float(gmx), 1.0f);
+        float y = recip_rn(s);
+        cast32_div<FMT, false>(v, s, y, 0, divisor_ok(s) && dividends_ok(st.mx, st.mn), out);
+        sc = __float_as_uint(s);
+    } else if (MODE == kModeMX) {
+        int e = mx_exponent<FMT>(__uint_as_float(st.mx));
+        cast32_mx<FMT>(v, -e, st.mx > 0x7F800000u, out);
+        sc = (uint32_t)(e + 127);
+    } else {  // MOSS
+        float s_i = __uint_as_float(st.mx) / fmt_max<FMT>();
+        int e = moss_exponent(u.s, s_i);
+        cast32_div<FMT, true>(v, u.s, u.y, -e, u.ok && dividends_ok(st.mx, st.mn) && e > -100, out);
+        sc = (uint32_t)(e + 127);
+    }
+}
+
+__device__ __forceinline__ void store32(uint8_t* p, const uint32_t* w) {
+    reinterpret_cast<uint4*>(p)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    reinterpret_cast<uint4*>(p)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
+__device__ __forceinline__ void block_reduce_atomic(uint32_t m, float* out) {
+    __shared__ uint32_t red[4];
+    m = wave_max_u32(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) atomicMax(reinterpret_cast<uint32_t*>(out), max(max(red[0], red[1]), max(red[2], red[3])));
+}
+
+// ------------------------------------------------------------------ row kernel
+// Output = input layout (rows x cols), cols % 32 == 0 (BLOCK: cols % 128 == 0).
+template <int FMT, int MODE, bool BF16, bool FUSED_AMAX, bool DERIVE>
+__global__ __launch_bounds__(256) void cast_rows_kernel(CastArgs a) {
+    const UniformScale u = uniform_scale<FMT, MODE, DERIVE>(a);
+    const int64_t cpr = a.cols / 32;
+    const int64_t total = a.rows * cpr;
+    const size_t esz = BF16 ? 2 : 4;
+    uint32_t tmax = 0;
+    for (int64_t base = (int64_t)blockIdx.x * 256; base < total; base += (int64_t)gridDim.x * 256) {
+        const int64_t g = base + threadIdx.x;
+        const bool valid = g < total;
+        const int64_t gg = valid ? g : total - 1;
+        const int64_t r = gg / cpr, c = gg - r * cpr;
+        const char* src = static_cast<const char*>(a.x) + (r * a.ld + c * 32) * esz;
+        float v[32];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) load8<BF16>(src + j * 8 * esz, v + 8 * j);
+        uint32_t out[8], sc = 0, cm = 0;
+        process_chunk<FMT, MODE>(v, u, out, sc, cm);
+        if (valid) {
+            store32(a.q + r * a.ldq + c * 32, out);
+            if (MODE == kModeBlock) {
+                if ((threadIdx.x & 3) == 0) reinterpret_cast<uint32_t*>(a.scales)[r * (a.cols / 128) + c / 4] = sc;
+            } else if (MODE == kModeMX || MODE == kModeMoss) {
+                reinterpret_cast<uint8_t*>(a.scales)[r * cpr + c] = (uint8_t)sc;
+            }
+            tmax = max(tmax, cm);
+        }
+    }
+    if (FUSED_AMAX) block_reduce_atomic(tmax, a.amax_out);
+}
+
+// ------------------------------------------------------------------ transposing kernel
+// Input tile 128 rows x 64 cols through LDS; output row = input column.  rows % 32 == 0
+// (BLOCK 1x128: rows % 128 == 0), cols % 8 == 0.
+template <int FMT, int MODE, bool BF16, bool FUSED_AMAX, bool DERIVE>
+__global__ __launch_bounds__(256) void cast_transposed_kernel(CastArgs a) {
+    __shared__ float tile[128][65];
+    const UniformScale u = uniform_scale<FMT, MODE, DERIVE>(a);
+    const int64_t r0 = (int64_t)blockIdx.y * 128, c0 = (int64_t)blockIdx.x * 64;
+    const size_t esz = BF16 ? 2 : 4;
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ch = t + 256 * i;
+        const int rr = ch >> 3, cc = (ch & 7) * 8;
+        float v[8];
+        if (r0 + rr < a.rows && c0 + cc < a.cols) {
+            load8<BF16>(static_cast<const char*>(a.x) + ((r0 + rr) * a.ld + c0 + cc) * esz, v);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) tile[rr][cc + k] = v[k];
+    }
+    __syncthreads();
+    const int oc = t >> 2, seg = t & 3;
+    float v[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) v[j] = tile[seg * 32 + j][oc];
+    uint32_t out[8], sc = 0, cm = 0;
+    process_chunk<FMT, MODE>(v, u, out, sc, cm);
+    const int64_t orow = c0 + oc, k0 = r0 + seg * 32;
+    if (orow < a.cols && k0 < a.rows) {
+        store32(a.q + orow * a.ldq + k0, out);
+        if (MODE == kModeBlock) {
+            if (seg == 0) reinterpret_cast<uint32_t*>(a.scales)[orow * (a.rows / 128) + r0 / 128] = sc;
+        } else if (MODE == kModeMX || MODE == kModeMoss) {
+            reinterpret_cast<uint8_t*>(a.scales)[orow * (a.rows / 32) + k0 / 32] = (uint8_t)sc;
+        }
+    }
+    if (FUSED_AMAX) block_reduce_atomic(cm, a.amax_out);
+}
+
+// ------------------------------------------------------------------ 128x128 weight blocks
+// One workgroup per 128x128 block (non-transposed, rows % 128 == 0, cols % 128 == 0): thread t
+// holds row t/2, columns (t%2)*64 .. +64 in registers; block amax via LDS; one pass over HBM.
+template <int FMT, bool BF16>
+__global__ __launch_bounds__(256) void cast_block128_kernel(CastArgs a) {
+    const int64_t br = blockIdx.y, bc = blockIdx.x;
+    const int t = threadIdx.x;
+    const int64_t r = br * 128 + (t >> 1), c = bc * 128 + (t & 1) * 64;
+    const size_t esz = BF16 ? 2 : 4;
+    const char* src = static_cast<const char*>(a.x) + (r * a.ld + c) * esz;
+    float v[64];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) load8<BF16>(src + j * 8 * esz, v + 8 * j);
+    ChunkStats s0 = chunk_stats(v), s1 = chunk_stats(v + 32);
+    uint32_t m = wave_max_u32(max(s0.mx, s1.mx));
+    __shared__ uint32_t red[4];
+    if ((t & 63) == 0) red[t >> 6] = m;
+    __syncthreads();
+    const uint32_t bm = max(max(red[0], red[1]), max(red[2], red[3]));
+    const float s = scale_from_amax<FMT>(__uint_as_float(bm), 1.0f);
+    const float y = recip_rn(s);
+    uint32_t out[16];
+    cast32_div<FMT, false>(v, s, y, 0, divisor_ok(s) && dividends_ok(s0.mx, s0.mn), out);
+    cast32_div<FMT, false>(v + 32, s, y, 0, divisor_ok(s) && dividends_ok(s1.mx, s1.mn), out + 8);
+    uint8_t* dst = a.q + r * a.ldq + c;
+    store32(dst, out);
+    store32(dst + 32, out + 8);
+    if (t == 0) reinterpret_cast<float*>(a.scales)[br * (a.cols / 128) + bc] = s;
+}
+
+// ------------------------------------------------------------------ generic exact fallback
+// One workgroup per output block (br x bc in output coordinates; TENSOR uses 1 x 256 tiles,
+// MX/MOSS 1 x 32).  Scalar loads, IEEE division, ragged edges with ceil semantics.
+template <int FMT, int MODE, bool BF16, bool FUSED_AMAX, bool DERIVE>
+__global__ __launch_bounds__(256) void cast_generic_kernel(CastArgs a, int br, int bc) {
+    const int64_t R = a.transpose ? a.cols : a.rows;   // output rows
+    const int64_t K = a.transpose ? a.rows : a.cols;   // output cols
+    const int64_t nbc = (K + bc - 1) / bc;
+    const int64_t bi = blockIdx.y, bj = blockIdx.x;
+    const int64_t rb = bi * br, kb = bj * bc;
+    const int64_t rn = min((int64_t)br, R - rb), kn = min((int64_t)bc, K - kb);
+    const int64_t n = rn * kn;
+    auto load = [&](int64_t i) -> float {
+        const int64_t orow = rb + i / kn, ok = kb + i % kn;
+        const int64_t ir = a.transpose ? ok : orow, ic = a.transpose ? orow : ok;
+        const int64_t idx = ir * a.ld + ic;
+        if (BF16) return bf16lo(static_cast<const uint16_t*>(a.x)[idx]);
+        return static_cast<const float*>(a.x)[idx];
+    };
+    __shared__ uint32_t red[4];
+    uint32_t m = 0;
+    for (int64_t i = threadIdx.x; i < n; i += 256) m = max(m, absbits(load(i)));
+    m = wave_max_u32(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    const uint32_t bm = max(max(red[0], red[1]), max(red[2], red[3]));
+    const float bamax = __uint_as_float(bm);
+    float s = 1.0f;
+    int shift = 0;
+    if (MODE == kModeTensor) {
+        s = DERIVE ? scale_from_amax<FMT>(*a.amax_in, 1.0f) : *a.scale_in;
+        if (DERIVE && bi == 0 && bj == 0 && threadIdx.x == 0) *a.scale_out = s;
+    } else if (MODE == kModeBlock) {
+        s = scale_from_amax<FMT>(bamax, 1.0f);
+        if (threadIdx.x == 0) reinterpret_cast<float*>(a.scales)[bi * nbc + bj] = s;
+    } else if (MODE == kModeMX) {
+        int e = mx_exponent<FMT>(bamax);
+        shift = -e;
+        if (threadIdx.x == 0) reinterpret_cast<uint8_t*>(a.scales)[bi * nbc + bj] = (uint8_t)(e + 127);
+    } else {
+        s = DERIVE ? scale_from_amax<FMT>(*a.amax_in, 1.0f) : *a.scale_in;
+        if (DERIVE && bi == 0 && bj == 0 && threadIdx.x == 0) *a.scale_out = s;
+        int e = moss_exponent(s, bamax / fmt_max<FMT>());
+        shift = -e;
+        if (threadIdx.x == 0) reinterpret_cast<uint8_t*>(a.scales)[bi * nbc + bj] = (uint8_t)(e + 127);
+    }
+    for (int64_t i = threadIdx.x; i < n; i += 256) {
+        float x = load(i);
+        float v = (MODE == kModeMX) ? x : x / s;
+        v = __builtin_amdgcn_ldexpf(v, shift);
+        a.q[(rb + i / kn) * a.ldq + kb + i % kn] = (uint8_t)code_slow<FMT>(v);
+    }
+    if (FUSED_AMAX && threadIdx.x == 0) atomicMax(reinterpret_cast<uint32_t*>(a.amax_out), bm);
+}
+
+// ------------------------------------------------------------------ dispatch
+template <int FMT, int MODE, bool BF16, bool FUSED, bool DERIVE>
+static void dispatch_shape(const CastArgs& a, hipStream_t st) {
+    const int64_t R = a.transpose ? a.cols : a.rows;
+    const int64_t K = a.transpose ? a.rows : a.cols;
+    if (R == 0 || K == 0) return;
+    if (!a.vec_out) {
+        int br = 1, bc = 32;
+        if (MODE == kModeTensor) { br = 1; bc = 256; }
+        if (MODE == kModeBlock) { br = a.block_r; bc = a.block_c; }
+        dim3 grid((unsigned)((K + bc - 1) / bc), (unsigned)((R + br - 1) / br));
+        hipLaunchKernelGGL((cast_generic_kernel<FMT, MODE, BF16, FUSED, DERIVE>), grid, dim3(256), 0, st, a, br, bc);
+        return;
+    }
+    const bool block128 = MODE == kModeBlock && a.block_r == 128 && a.block_c == 128;
+    const bool row_group_ok = MODE != kModeBlock || (a.block_r == 1 && a.block_c == 128);
+    if (!a.transpose) {
+        if (block128 && !FUSED && a.rows % 128 == 0 && a.cols % 128 == 0) {
+            hipLaunchKernelGGL((cast_block128_kernel<FMT, BF16>), dim3((unsigned)(a.cols / 128), (unsigned)(a.rows / 128)),
+                               dim3(256), 0, st, a);
+            return;
+        }
+        const int64_t kmod = MODE == kModeBlock ? 128 : 32;
+        if (row_group_ok && a.cols % kmod == 0) {
+            int64_t total = a.rows * (a.cols / 32);
+            int64_t blocks = (total + 255) / 256;
+            int64_t cap = FUSED ? kMaxReduceBlocks : 8192;
+            if (blocks > cap) blocks = cap;
+            hipLaunchKernelGGL((cast_rows_kernel<FMT, MODE, BF16, FUSED, DERIVE>), dim3((unsigned)blocks), dim3(256), 0,
+                               st, a);
+            return;
+        }
+    } else {
+        const int64_t kmod = MODE == kModeBlock ? 128 : 32;
+        if (row_group_ok && a.rows % kmod == 0 && a.cols % 8 == 0) {
+            dim3 grid((unsigned)((a.cols + 63) / 64), (unsigned)((a.rows + 127) / 128));
+            hipLaunchKernelGGL((cast_transposed_kernel<FMT, MODE, BF16, FUSED, DERIVE>), grid, dim3(256), 0, st, a);
+            return;
+        }
+    }
+    int br = 1, bc = 32;
+    if (MODE == kModeTensor) { br = 1; bc = 256; }
+    if (MODE == kModeBlock) { br = a.block_r; bc = a.block_c; }
+    dim3 grid((unsigned)((K + bc - 1) / bc), (unsigned)((R + br - 1) / br));
+    hipLaunchKernelGGL((cast_generic_kernel<FMT, MODE, BF16, FUSED, DERIVE>), grid, dim3(256), 0, st, a, br, bc);
+}
+
+template <int FMT, int MODE, bool BF16>
+static void dispatch_flags(const CastArgs& a, hipStream_t st) {
+    const bool derive = a.amax_in != nullptr;
+    const bool fused = a.amax_out != nullptr && MODE == kModeTensor && !derive;
+    if (MODE == kModeTensor || MODE == kModeMoss) {
+        if (derive) dispatch_shape<FMT, MODE, BF16, false, true>(a, st);
+        else if (fused) dispatch_shape<FMT, MODE, BF16, true, false>(a, st);
+        else dispatch_shape<FMT, MODE, BF16, false, false>(a, st);
+    } else {
+        dispatch_shape<FMT, MODE, BF16, false, false>(a, st);
+    }
+}
+
+template <int FMT, int MODE>
+static void dispatch_in(const CastArgs& a, hipStream_t st) {
+    if (a.bf16) dispatch_flags<FMT, MODE, true>(a, st);
+    else dispatch_flags<FMT, MODE, false>(a, st);
+}
+
+template <int FMT>
+static void dispatch_mode(const CastArgs& a, hipStream_t st) {
+    switch (a.mode) {
+        case kModeTensor: dispatch_in<FMT, kModeTensor>(a, st); break;
+        case kModeBlock: dispatch_in<FMT, kModeBlock>(a, st); break;
+        case kModeMX: dispatch_in<FMT, kModeMX>(a, st); break;
+        default: dispatch_in<FMT, kModeMoss>(a, st); break;
+    }
+}
+
+int launch_cast(const CastArgs& a, hipStream_t st) {
+    if (a.fmt == kE4M3) dispatch_mode<kE4M3>(a, st);
+    else dispatch_mode<kE5M2>(a, st);
+    return 0;
+}
+
+}  // namespace fp8q

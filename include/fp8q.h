@@ -1,0 +1,174 @@
+/*
+ * fp8q.h -- C ABI of the FP8 quantize-then-scaled-GEMM library for AMD Instinct MI355X (gfx950).
+ *
+ * The computation: an amax reduction, a saturating round-to-nearest-even cast to OCP FP8 (E4M3 for
+ * activations and weights, E5M2 for gradients) under one of five scaling schemes, and a GEMM over
+ * the FP8 operands with FP32 accumulation and dequantisation by the scales.
+ *
+ * Sources (by page title and section):
+ *  [FLAX] "Flax FP8 量化实战指南：从 fp8_ops 低层 API 到 Fp8DotGeneral / Fp8Einsum 的完整实现解析":
+ *         section 1 (Q/DQ: scale = amax/MAX, x_fp8 = clip(x/scale), x ~= x_fp8 * scale),
+ *         section 2.2 (current scaling; quantize = divide, clip to +-MAX, cast; FP32-accumulated
+ *         dot; dequantize by a_scale * b_scale), section 2.3 (delayed scaling with an amax history).
+ *  [NANO] "Nanochat的FP8训练模块", section "实现" (E4M3/E5M2 and their maxima; the three GEMMs of a
+ *         linear layer's forward and backward; output dtype always given explicitly; operand-layout
+ *         bookkeeping is where transposes silently go wrong).
+ *  [HF]   "Transformers 中的细粒度 FP8 量化配置、DeepGEMM 加速路径与 UE8M0 缩放格式完全指南":
+ *         section 一 (128x128 weight blocks, 1x128 per-token activation groups, weight_scale_inv
+ *         of shape (ceil(out/128), ceil(in/128))), section 四 (block size is two positive ints).
+ *  [MOSS] "MOSS:高效、精确的 FP8 LLM 训练,采用微尺度和自动尺度变换": section 1 (MXFP8: one
+ *         power-of-two scale per 32 consecutive values), section 4 (two-level scaling: FP32 global
+ *         factor = max of the per-32 factors, E8M0 local factor per 32 values, FP32 factors applied
+ *         once in the GEMM epilogue).
+ *
+ * Conventions for every entry point:
+ *  - All data pointers are DEVICE pointers owned by the caller.  The library never allocates or
+ *    frees, never synchronizes, and enqueues all work on `stream` (a hipStream_t passed as void*;
+ *    NULL means the default stream).  Results are ready when the stream's work completes.
+ *  - Every call returns an fp8q_status and never throws.  On a non-OK return nothing has been
+ *    enqueued (argument errors) or the HIP error is reported (FP8Q_ERR_HIP); fp8q_last_error()
+ *    gives a message for the calling thread.
+ *  - Scales at the boundary are dequantisation multipliers everywhere: x ~= decode(q) * scale.
+ *  - FP8 bytes are OCP e4m3fn (bias 7, max 448, no Inf, NaN = S.1111.111) and e5m2 (bias 15,
+ *    max 57344).  E8M0 bytes hold e + 127 for a scale of 2^e.
+ *  - Matrices are row-major with a leading dimension in elements (`ld`); every row pointer
+ *    (base + r*ld*elem_size) must be 16-byte aligned.
+ *  - Calls that share output buffers must be ordered by the caller (same stream or events).
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FP8Q_OK = 0,
+    FP8Q_ERR_INVALID_ARG = -1,   /* bad enum, shape, block size, alignment or NULL pointer */
+    FP8Q_ERR_UNSUPPORTED = -2,   /* a valid request outside what the kernels implement */
+    FP8Q_ERR_HIP = -3,           /* a HIP runtime call or kernel launch failed */
+    FP8Q_ERR_NO_DEVICE = -4      /* no gfx950 device is current */
+} fp8q_status;
+
+typedef enum { FP8Q_E4M3 = 0, FP8Q_E5M2 = 1 } fp8q_fmt;
+typedef enum { FP8Q_IN_F32 = 0, FP8Q_IN_BF16 = 1 } fp8q_in;
+typedef enum { FP8Q_OUT_F32 = 0, FP8Q_OUT_BF16 = 1 } fp8q_out;
+typedef enum {
+    FP8Q_TENSOR = 0,   /* one fp32 scale for the tensor (current, delayed or static) */
+    FP8Q_BLOCK = 1,    /* one fp32 scale per (block_r x block_c) block */
+    FP8Q_MX = 2,       /* one E8M0 scale per 32 consecutive values along K */
+    FP8Q_MOSS = 3      /* fp32 global factor S times one E8M0 local factor per 32 values along K */
+} fp8q_mode;
+
+/* Checks that the current device is gfx950.  Called implicitly by every entry point; returns
+ * FP8Q_ERR_NO_DEVICE otherwise. */
+int fp8q_init(void);
+
+/* Message describing the calling thread's last non-OK status ("" if none). */
+const char* fp8q_last_error(void);
+
+/*
+ * fp8_amax -- amax = max |x| over a rows x cols matrix ([FLAX] section 1).
+ *   x         rows x cols, fp32 or bf16 (`in_dtype`), leading dimension ld >= cols.
+ *   amax_out  one fp32 on the device.  It is overwritten (not accumulated into).  Any NaN in x
+ *             gives NaN; -0 counts as 0; an empty matrix gives 0.
+ * The reduction is an integer max over the sign-cleared bit patterns, so it is exact and
+ * independent of reduction order.
+ */
+int fp8_amax(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld,
+             float* amax_out, void* stream);
+
+/*
+ * fp8_quantize -- saturating round-to-nearest-even FP8 cast under one scaling scheme.
+ *
+ * The logical operand is x (rows x cols, leading dimension ld, fp32 or bf16).  With
+ * transpose_out = 0 the output q is rows x cols; with transpose_out = 1 it is cols x rows
+ * (q[c][r] quantizes x[r][c]).  "K" is the last axis of the OUTPUT: scale groups run along it.
+ * ldq is q's leading dimension in bytes.  Every element is
+ *     q = RNE8( clip( fl(x / scale), -MAX, +MAX ) )       with fl() one IEEE fp32 division,
+ * MAX = 448 (E4M3) or 57344 (E5M2); NaN inputs give S.1111111 with the input's sign.
+ *
+ * mode FP8Q_TENSOR ([FLAX] sections 2.2, 2.3):
+ *   scale_is_input = 1: *tensor_scale (device fp32) is the scale to use (delayed or static
+ *     scaling); it is not modified.  If amax_out is non-NULL the amax of x is computed in the same
+ *     pass and written to *amax_out (the value fp8_history_update consumes).
+ *   scale_is_input = 0: current scaling.  amax_out must be non-NULL; the call writes
+ *     amax = max|x| to *amax_out, scale = fl(amax / MAX) to *tensor_scale (1.0 when amax is 0,
+ *     non-finite, or the quotient underflows to 0), then quantizes with it.
+ *   scales, block_r, block_c are ignored.
+ * mode FP8Q_BLOCK ([HF] section 一): one fp32 scale per (block_r x block_c) block of the OUTPUT,
+ *   scale = fl(amax_block / MAX) (1.0 on zero/non-finite/underflow), written to `scales` as
+ *   fp32[ceil(R/block_r)][ceil(K/block_c)] row-major (R, K = output rows, cols).
+ *   (1,128) is the per-token activation scheme, (128,128) the weight scheme; both must be positive
+ *   ([HF] section 四).  tensor_scale and scale_is_input are ignored; amax_out may be NULL.
+ * mode FP8Q_MX ([MOSS] section 1): per group of 32 along K, e = smallest integer in [-127, 127]
+ *   with MAX * 2^e >= amax_group (127 if none, e.g. a non-finite group), E8M0 byte e + 127 written
+ *   to `scales` as u8[R][ceil(K/32)]; element = RNE8(clip(fl(x * 2^-e))).  block_r/block_c,
+ *   tensor_scale and scale_is_input are ignored.
+ * mode FP8Q_MOSS ([MOSS] section 4): global S = fl(amax_tensor / MAX) (1.0 on zero/non-finite/
+ *   underflow); per group i of 32 along K, s_i = fl(amax_i / MAX) and e_i = smallest integer in
+ *   [-127, 0] with S * 2^e_i >= s_i (0 if none), E8M0 byte e_i + 127 in `scales` u8[R][ceil(K/32)];
+ *   element = RNE8(clip(fl(fl(x / S) * 2^-e_i))).  scale_is_input = 0: amax_out must be non-NULL,
+ *   receives amax_tensor, and S is written to *tensor_scale.  scale_is_input = 1: *tensor_scale
+ *   holds S (from an earlier call on the same source tensor, e.g. the other copy of a
+ *   forward/backward pair) and is not modified.
+ *
+ * Limits (FP8Q_ERR_UNSUPPORTED otherwise): cols % 8 == 0, ld % 8 == 0 and a 16-byte aligned x.
+ * Any ldq >= K works (ldq % 16 == 0 with a 16-byte aligned q selects the vectorized kernels).
+ * Ragged group tails (K not a multiple of the group) are handled with ceil semantics.
+ */
+int fp8_quantize(int mode, int fmt, const void* x, int in_dtype,
+                 int64_t rows, int64_t cols, int64_t ld,
+                 int block_r, int block_c, int transpose_out,
+                 uint8_t* q, int64_t ldq, void* scales,
+                 float* tensor_scale, int scale_is_input, float* amax_out,
+                 void* stream);
+
+/*
+ * fp8_history_update -- delayed-scaling state update ([FLAX] section 2.3), called after the cast
+ * of step t with that step's amax a_t:
+ *     history <- roll(history, -1) with history[0] = *amax_new   (newest at index 0)
+ *     *scale_inout <- fl(max(history) / MAX), or unchanged if that max is 0, non-finite or the
+ *                     quotient underflows.
+ * history: device fp32[len], 1 <= len <= 4096 (the pages use 1024, initialised to zeros with the
+ * scale initialised to 1).  The scale left in *scale_inout is the one step t+1 quantizes with,
+ * which is exactly the scale Flax's in-step order computes at step t+1.
+ */
+int fp8_history_update(float* history, int64_t len, const float* amax_new,
+                       float* scale_inout, int fmt, void* stream);
+
+/*
+ * fp8_scaled_gemm -- C = dequant(A) . dequant(B)^T with FP32 accumulation.
+ *   A: M x K FP8 bytes (format afmt), leading dimension lda bytes.  B: N x K FP8 bytes (bfmt),
+ *   leading dimension ldb bytes -- both K-contiguous, so C = A B^T; a K x N operand is brought
+ *   to N x K once by fp8_quantize(..., transpose_out = 1) ([NANO] on layout bookkeeping).
+ *   C: M x N, fp32 or bf16 (`out_dtype`, required, round-to-nearest-even), leading dimension ldc
+ *   elements.
+ * Scale arguments by mode:
+ *   FP8Q_TENSOR: Aglobal = &s_a, Bglobal = &s_b (device fp32); C = (sum qa*qb) * fl(s_a * s_b)
+ *                ([FLAX] section 2.2).  Ascale, Bscale unused.
+ *   FP8Q_BLOCK:  Ascale fp32[M][ceil(K/128)] (1x128 per token), Bscale fp32[ceil(N/128)][ceil(K/128)]
+ *                (128x128 weight blocks, [HF] section 一); every 128-wide K block's FP32 partial
+ *                sum is scaled by fl(sa[m][kb] * sb[n/128][kb]) and accumulated in the main loop.
+ *   FP8Q_MX:     Ascale u8 E8M0[M][ceil(K/32)], Bscale u8 E8M0[N][ceil(K/32)]; the power-of-two
+ *                scales are applied by the matrix-core instruction ([MOSS] section 1).
+ *   FP8Q_MOSS:   as MX, plus Aglobal = &S_A, Bglobal = &S_B applied once in the epilogue as
+ *                fl(S_A * S_B) ([MOSS] section 4).
+ * Accumulation: each 128-wide K chunk is reduced by the FP8 matrix instruction from zero and its
+ * FP32 result is added into an FP32 accumulator (a full-precision accumulation every 128 K).
+ * Limits (FP8Q_ERR_UNSUPPORTED otherwise): K % 16 == 0, lda/ldb % 16 == 0, 16-byte aligned A, B.
+ * M, N, K need not be multiples of any tile size.
+ */
+int fp8_scaled_gemm(int mode, const uint8_t* A, int afmt, const void* Ascale,
+                    const uint8_t* B, int bfmt, const void* Bscale,
+                    const float* Aglobal, const float* Bglobal,
+                    int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                    void* C, int out_dtype, int64_t ldc, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8Q_H */

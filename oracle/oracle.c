@@ -261,16 +261,12 @@ void orc_quantize_mx(const void* x, int in_kind, int64_t rows, int64_t cols, int
     free(t);
 }
 
-/* MOSS two-level scaling.  Step 1: s_i = fl(amax_i / MAX) per group of 32 along the last axis.
- * Step 2: global S = fl(amax_tensor / MAX) (= max_i s_i; fallback 1).  Step 3: local exponent
- * e_i = smallest e in [-127, 0] with S * 2^e >= s_i, stored as E8M0 byte e_i + 127.
- * Step 4: element encode(clip(fl(fl(x/S) * 2^-e_i))), so x ~= q * S * 2^e_i.  [MOSS] section 4 */
-void orc_quantize_moss(const void* x, int in_kind, int64_t rows, int64_t cols, int64_t ld, int fmt,
-                       int transpose, uint8_t* q, int64_t ldq, uint8_t* e8m0, float* S_out) {
+/* MOSS two-level scaling with a given global factor S (steps 1, 3 and 4 below); used directly
+ * for the second quantized copy of a tensor whose S is already known. */
+void orc_quantize_moss_given(const void* x, int in_kind, int64_t rows, int64_t cols, int64_t ld, int fmt,
+                             int transpose, float S, uint8_t* q, int64_t ldq, uint8_t* e8m0) {
     int64_t R, C;
     float* t = logical_f32(x, in_kind, rows, cols, ld, transpose, &R, &C);
-    float S = orc_compute_scale(amax_f32(t, C, 0, R, 0, C), fmt, 1.0f);
-    *S_out = S;
     int64_t ng = (C + 31) / 32;
     float M = (float)orc_fp8_max(fmt);
     #pragma omp parallel for schedule(static)
@@ -288,6 +284,17 @@ void orc_quantize_moss(const void* x, int in_kind, int64_t rows, int64_t cols, i
         }
     }
     free(t);
+}
+
+/* MOSS two-level scaling.  Step 1: s_i = fl(amax_i / MAX) per group of 32 along the last axis.
+ * Step 2: global S = fl(amax_tensor / MAX) (= max_i s_i; fallback 1).  Step 3: local exponent
+ * e_i = smallest e in [-127, 0] with S * 2^e >= s_i, stored as E8M0 byte e_i + 127.
+ * Step 4: element encode(clip(fl(fl(x/S) * 2^-e_i))), so x ~= q * S * 2^e_i.  [MOSS] section 4 */
+void orc_quantize_moss(const void* x, int in_kind, int64_t rows, int64_t cols, int64_t ld, int fmt,
+                       int transpose, uint8_t* q, int64_t ldq, uint8_t* e8m0, float* S_out) {
+    float S = orc_compute_scale(orc_amax(x, in_kind, rows, cols, ld), fmt, 1.0f);
+    *S_out = S;
+    orc_quantize_moss_given(x, in_kind, rows, cols, ld, fmt, transpose, S, q, ldq, e8m0);
 }
 
 /* ---------------------------------------------------------------- delayed ---- */

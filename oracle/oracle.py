@@ -54,6 +54,7 @@ def lib():
             "orc_quantize_block": (None, [P, I, I64, I64, I64, I, I64, I64, I, P, I64, P]),
             "orc_quantize_mx": (None, [P, I, I64, I64, I64, I, I, P, I64, P]),
             "orc_quantize_moss": (None, [P, I, I64, I64, I64, I, I, P, I64, P, P]),
+            "orc_quantize_moss_given": (None, [P, I, I64, I64, I64, I, I, F, P, I64, P]),
             "orc_history_roll_insert": (None, [P, I64, F]),
             "orc_history_max": (F, [P, I64]),
             "orc_delayed_step": (None, [P, I, I64, I64, I64, I, I, P, P, I64, P, I64, P]),
@@ -175,6 +176,17 @@ def quantize_moss(x: np.ndarray, fmt: int, transpose: bool = False):
     lib().orc_quantize_moss(_p(x), kind, x.shape[0], x.shape[1], x.shape[1], fmt, int(transpose),
                             _p(q), C, _p(e), _p(S))
     return q, e, S[0]
+
+
+def quantize_moss_given(x: np.ndarray, fmt: int, S: float, transpose: bool = False):
+    """MOSS elements and local exponents for a known global factor S (e.g. a row sample)."""
+    x, kind = _input(x)
+    R, C = _out_shape(x, transpose)
+    q = np.empty((R, C), np.uint8)
+    e = np.empty((R, (C + 31) // 32), np.uint8)
+    lib().orc_quantize_moss_given(_p(x), kind, x.shape[0], x.shape[1], x.shape[1], fmt, int(transpose),
+                                  float(S), _p(q), C, _p(e))
+    return q, e
 
 
 # ------------------------------------------------------------------ delayed scaling

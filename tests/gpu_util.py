@@ -1,0 +1,121 @@
+"""Helpers shared by the GPU parity tests: host<->device transfer of the seeded inputs, oracle-side
+dequantization of row samples, and the GEMM error bound.
+
+GEMM tolerance.  The oracle's reference is the exact (fp64) product of the dequantized operands.
+The library reduces each 128-wide K chunk with gfx950's FP8 matrix instruction and adds the FP32
+result into an FP32 accumulator.  Measured on the hardware, one such instruction's result differs
+from the exact sum of its products by at most 2^-11.1 times the largest product magnitude in the
+chunk (over 2048 x 256 random chunks, with and without outliers and scales); FP32 accumulation,
+the block-scale product fl(sx*sw) and the epilogue factor each add at most one unit roundoff
+(2^-24) of D = sum_k |a_k b_k| per operation.  The elementwise bound used in the tests is therefore
+    |C - C_ref| <= 2^-10 * E + (K/128 + 3) * 2^-24 * D,
+with E = sum over 128-wide K chunks of max_k |a_k b_k| (a factor-2 margin on the measured 2^-11.1).
+The bf16 output must equal round-to-nearest-even of the same kernel's fp32 output bit for bit, and
+its normwise relative error must stay within 2e-3.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from fp8_scaled_quantization_amd import workloads
+
+DEV = "cuda:0"
+
+
+def to_dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def to_dev(x: np.ndarray) -> torch.Tensor:
+    if x.dtype == np.uint16:
+        return to_dev_bf16(x)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def same(got: np.ndarray, want: np.ndarray, label: str = "", show: int = 6) -> bool:
+    """Bitwise equality that prints the count and the first mismatching positions on failure."""
+    got = np.asarray(got)
+    want = np.asarray(want)
+    if got.shape != want.shape:
+        print("%s: shape %s != %s" % (label, got.shape, want.shape))
+        return False
+    gb = got.view(np.uint8) if got.dtype != np.uint8 else got
+    wb = want.view(np.uint8) if want.dtype != np.uint8 else want
+    if got.dtype == want.dtype and np.array_equal(gb, wb):
+        return True
+    bad = np.argwhere(got != want) if got.dtype != np.float32 else np.argwhere(
+        got.view(np.uint32) != want.astype(np.float32).view(np.uint32))
+    print("%s: %d mismatches of %d" % (label, len(bad), got.size))
+    for idx in bad[:show]:
+        i = tuple(int(v) for v in idx)
+        print("   at %s: got %r want %r" % (i, got[i], want[i]))
+    return False
+
+
+def bf16_rne_bits(x32: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bits by torch's round-to-nearest-even (an independent library conversion)."""
+    return workloads.to_bf16_bits(x32)
+
+
+def chunk_max_sum(A: np.ndarray, B: np.ndarray, pairs=None, chunk: int = 128):
+    """E[m,n] = sum over K chunks of max |A[m,k] B[n,k]| (full matrix or for the listed pairs)."""
+    K = A.shape[1]
+    nck = -(-K // chunk)
+    pad = nck * chunk - K
+    if pad:
+        A = np.pad(A, ((0, 0), (0, pad)))
+        B = np.pad(B, ((0, 0), (0, pad)))
+    if pairs is not None:
+        out = np.empty(len(pairs))
+        for i0 in range(0, len(pairs), 256):
+            p = pairs[i0:i0 + 256]
+            prod = np.abs(A[p[:, 0]] * B[p[:, 1]]).reshape(len(p), nck, chunk)
+            out[i0:i0 + 256] = prod.max(axis=2).sum(axis=1)
+        return out
+    M, N = A.shape[0], B.shape[0]
+    E = np.empty((M, N))
+    Ar = np.abs(A).reshape(M, nck, chunk)
+    Br = np.abs(B).reshape(N, nck, chunk)
+    for m in range(M):
+        E[m] = (Ar[m][None, :, :] * Br).max(axis=2).sum(axis=1)
+    return E
+
+
+def gemm_bound(E, D, K):
+    return 2.0 ** -10 * E + (K / 128.0 + 3.0) * 2.0 ** -24 * D
+
+
+def check_gemm(C32: np.ndarray, Cbf: np.ndarray | None, Cref: np.ndarray, D: np.ndarray, E: np.ndarray, K: int,
+               label: str = ""):
+    """Assert the elementwise bound on the fp32 output, bf16 == RNE(fp32), normwise bf16 error."""
+    err = np.abs(C32.astype(np.float64) - Cref)
+    bound = gemm_bound(E, D, K)
+    bad = err > bound
+    assert not bad.any(), "%s: %d of %d outputs exceed the bound; worst err/bound %.3g" % (
+        label, int(bad.sum()), bad.size, float((err / np.maximum(bound, 1e-300)).max()))
+    if Cbf is not None:
+        assert np.array_equal(Cbf, bf16_rne_bits(C32)), "%s: bf16 output is not RNE(fp32 output)" % label
+        cb = workloads.bf16_bits_to_f32(Cbf).astype(np.float64)
+        nrm = np.linalg.norm(Cref)
+        if nrm > 0:
+            assert np.linalg.norm(cb - Cref) / nrm <= 2e-3, label
+    return float((err / np.maximum(bound, 1e-300)).max())
+
+
+def sample_pairs(M: int, N: int, n: int, seed: int, tile: int = 128) -> np.ndarray:
+    """Seeded (m, n) sample: random pairs plus rows/cols on every tile edge and the last row/col."""
+    rng = np.random.default_rng(seed)
+    pairs = [np.stack([rng.integers(0, M, n), rng.integers(0, N, n)], 1)]
+    edges_m = np.unique(np.clip(np.concatenate([np.arange(0, M, tile), np.arange(tile - 1, M, tile), [M - 1]]), 0, M - 1))
+    edges_n = np.unique(np.clip(np.concatenate([np.arange(0, N, tile), np.arange(tile - 1, N, tile), [N - 1]]), 0, N - 1))
+    pairs.append(np.stack([edges_m, rng.integers(0, N, len(edges_m))], 1))
+    pairs.append(np.stack([rng.integers(0, M, len(edges_n)), edges_n], 1))
+    return np.concatenate(pairs).astype(np.int64)

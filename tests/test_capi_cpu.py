@@ -1,0 +1,57 @@
+"""CPU checks of the C ABI library: it loads, exports every entry point declared in include/fp8q.h,
+and rejects invalid arguments with the documented status codes before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from fp8_scaled_quantization_amd import _lib
+    return _lib
+
+
+def test_exports_match_header(L):
+    hdr = open(os.path.join(ROOT, "include", "fp8q.h")).read()
+    declared = set(re.findall(r"^(?:int|const char\*)\s+(\w+)\(", hdr, re.M))
+    assert declared == set(L.EXPORTS)
+    for name in declared:
+        assert hasattr(L.lib(), name)
+
+
+def _err(L):
+    return L.lib().fp8q_last_error().decode()
+
+
+def test_invalid_arguments(L):
+    lib = L.lib()
+    dummy = ctypes.c_void_p(16)
+    # unknown mode / format / dtype
+    assert lib.fp8_quantize(7, 0, dummy, 1, 4, 8, 8, 1, 128, 0, dummy, 16, dummy, dummy, 1, None, None) == L.ERR_INVALID_ARG
+    assert "mode" in _err(L)
+    assert lib.fp8_quantize(0, 5, dummy, 1, 4, 8, 8, 1, 128, 0, dummy, 16, dummy, dummy, 1, None, None) == L.ERR_INVALID_ARG
+    assert lib.fp8_quantize(0, 0, dummy, 9, 4, 8, 8, 1, 128, 0, dummy, 16, dummy, dummy, 1, None, None) == L.ERR_INVALID_ARG
+    # block sizes must be two positive integers
+    assert lib.fp8_quantize(1, 0, dummy, 1, 4, 8, 8, 0, 128, 0, dummy, 16, dummy, None, 0, None, None) == L.ERR_INVALID_ARG
+    assert "positive" in _err(L)
+    # derived scale needs amax_out; TENSOR needs tensor_scale
+    assert lib.fp8_quantize(0, 0, dummy, 1, 4, 8, 8, 1, 128, 0, dummy, 16, None, dummy, 0, None, None) == L.ERR_INVALID_ARG
+    assert lib.fp8_quantize(0, 0, dummy, 1, 4, 8, 8, 1, 128, 0, dummy, 16, None, None, 1, None, None) == L.ERR_INVALID_ARG
+    # alignment / multiples outside the kernels' limits
+    assert lib.fp8_quantize(0, 0, dummy, 1, 4, 12, 12, 1, 128, 0, dummy, 16, None, dummy, 1, None, None) == L.ERR_UNSUPPORTED
+    # ld smaller than cols
+    assert lib.fp8_amax(dummy, 1, 4, 16, 8, dummy, None) == L.ERR_INVALID_ARG
+    # history length bounds
+    assert lib.fp8_history_update(dummy, 0, dummy, dummy, 0, None) == L.ERR_INVALID_ARG
+    assert lib.fp8_history_update(dummy, 5000, dummy, dummy, 0, None) == L.ERR_INVALID_ARG
+    # GEMM: out_dtype is required, globals for TENSOR, scales for MX
+    g = lib.fp8_scaled_gemm
+    assert g(0, dummy, 0, None, dummy, 0, None, dummy, dummy, 16, 16, 32, 32, 32, dummy, 7, 16, None) == L.ERR_INVALID_ARG
+    assert "out_dtype" in _err(L)
+    assert g(0, dummy, 0, None, dummy, 0, None, None, None, 16, 16, 32, 32, 32, dummy, 0, 16, None) == L.ERR_INVALID_ARG
+    assert g(2, dummy, 0, None, dummy, 0, None, None, None, 16, 16, 32, 32, 32, dummy, 0, 16, None) == L.ERR_INVALID_ARG
+    assert g(0, dummy, 0, None, dummy, 0, None, dummy, dummy, 16, 16, 24, 32, 32, dummy, 0, 16, None) == L.ERR_UNSUPPORTED

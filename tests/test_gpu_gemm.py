@@ -1,0 +1,180 @@
+"""GPU parity of the scaled FP8 GEMM against the oracle's fp64 product of the same quantized
+operands, with the elementwise bound derived in tests/gpu_util.py: full comparison on small and
+ragged shapes (several tiles and partial tiles), and sampled outputs at the five workloads' full
+shapes in the launch configuration the benchmark times."""
+import numpy as np
+import pytest
+import torch
+
+from fp8_scaled_quantization_amd import workloads
+from tests.gpu_util import DEV, check_gemm, chunk_max_sum, host, sample_pairs, to_dev
+
+pytestmark = pytest.mark.gpu
+
+E4M3, E5M2 = 0, 1
+TENSOR, BLOCK, MX, MOSS = 0, 1, 2, 3
+OUT_F32, OUT_BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def fq():
+    import fp8_scaled_quantization_amd as fq
+    fq.init()
+    return fq
+
+
+def _quant_operand(fq, orc, x, mode, fmt, block, transpose=False, S=None):
+    """Quantize on the GPU; return device tensors and the oracle's fp64 dequantized operand built
+    from the GPU's bytes and scales (the casts themselves are checked bit-exactly elsewhere)."""
+    xd = to_dev(x)
+    if mode == MOSS and S is not None:
+        q, sc, g, _ = fq.quantize(xd, mode, fmt, transpose_out=transpose, tensor_scale=S, scale_is_input=True)
+    else:
+        q, sc, g, _ = fq.quantize(xd, mode, fmt, block=block or (1, 128), transpose_out=transpose)
+    hq = host(q)
+    hs = host(sc) if sc is not None else None
+    hg = np.float32(host(g)[0]) if g is not None else None
+    return (q, sc, g), (hq, hs, hg)
+
+
+def _deq(orc, mode, hq, hs, hg, fmt, block):
+    return orc.dequantize(mode, hq, fmt, hs, hg, block=block)
+
+
+def _run(fq, mode, A, afmt, B, bfmt, out):
+    (qa, sa, ga), (qb, sb, gb) = A, B
+    return fq.scaled_gemm(mode, qa, afmt, sa, qb, bfmt, sb, ga, gb, out_dtype=out)
+
+
+SMALL = [(200, 136, 384), (128, 128, 128), (256, 384, 1024), (16, 64, 32), (300, 260, 272)]
+
+
+@pytest.mark.parametrize("mode", [TENSOR, BLOCK, MX, MOSS])
+@pytest.mark.parametrize("M,N,K", SMALL)
+@pytest.mark.parametrize("fmts", [(E4M3, E4M3), (E5M2, E4M3), (E4M3, E5M2)])
+def test_gemm_small_full(fq, orc, mode, M, N, K, fmts):
+    if mode == BLOCK and K % 128:
+        K = (K + 127) // 128 * 128
+    afmt, bfmt = fmts
+    xa = workloads.random_matrix(M * 3 + K, M, K, 2.0)
+    xb = workloads.random_matrix(N * 5 + K, N, K, 0.05)
+    ba, bb = ((1, 128), (128, 128)) if mode == BLOCK else ((1, 128), (1, 128))
+    A, (hqa, hsa, hga) = _quant_operand(fq, orc, xa, mode, afmt, ba)
+    B, (hqb, hsb, hgb) = _quant_operand(fq, orc, xb, mode, bfmt, bb)
+    Ad = _deq(orc, mode, hqa, hsa, hga, afmt, ba)
+    Bd = _deq(orc, mode, hqb, hsb, hgb, bfmt, bb)
+    Cref, D = orc.gemm_ref(Ad, Bd)
+    E = chunk_max_sum(Ad, Bd)
+    C32 = host(_run(fq, mode, A, afmt, B, bfmt, OUT_F32))
+    Cbf = host(_run(fq, mode, A, afmt, B, bfmt, OUT_BF16))
+    check_gemm(C32, Cbf, Cref, D, E, K, "mode %d %dx%dx%d" % (mode, M, N, K))
+
+
+def test_gemm_per_tensor_small_exact_config(fq, orc):
+    """16x32 @ 32x64 fp32 U[0,1): all products are non-negative, so D = |C_ref| and the bound is
+    relative to C_ref itself."""
+    a, b = workloads.per_tensor_inputs()
+    A, (hqa, _, hga) = _quant_operand(fq, orc, a, TENSOR, E4M3, None)
+    B, (hqb, _, hgb) = _quant_operand(fq, orc, b, TENSOR, E4M3, None, transpose=True)
+    Ad = orc.dequantize(TENSOR, hqa, E4M3, None, hga)
+    Bd = orc.dequantize(TENSOR, hqb, E4M3, None, hgb)
+    Cref, D = orc.gemm_ref(Ad, Bd)
+    C32 = host(_run(fq, TENSOR, A, E4M3, B, E4M3, OUT_F32))
+    worst = check_gemm(C32, None, Cref, D, chunk_max_sum(Ad, Bd), 32, "16x32x64")
+    assert np.allclose(D, np.abs(Cref))
+    assert np.max(np.abs(C32 - Cref) / np.abs(Cref)) < 1e-3 and worst <= 1.0
+
+
+def test_gemm_delayed_step_full(fq, orc):
+    """One delayed-scaling step at 1024x2048 @ 2048x1024, full output comparison."""
+    Araw, Braw, _ = workloads.delayed_inputs(3)
+    A, (hqa, _, hga) = _quant_operand(fq, orc, Araw, TENSOR, E4M3, None)
+    B, (hqb, _, hgb) = _quant_operand(fq, orc, Braw, TENSOR, E4M3, None, transpose=True)
+    Ad = orc.dequantize(TENSOR, hqa, E4M3, None, hga)
+    Bd = orc.dequantize(TENSOR, hqb, E4M3, None, hgb)
+    Cref, D = orc.gemm_ref(Ad, Bd)
+    E = chunk_max_sum(Ad, Bd)
+    C32 = host(_run(fq, TENSOR, A, E4M3, B, E4M3, OUT_F32))
+    Cbf = host(_run(fq, TENSOR, A, E4M3, B, E4M3, OUT_BF16))
+    check_gemm(C32, Cbf, Cref, D, E, 2048, "delayed 1024x1024x2048")
+
+
+def _sampled_check(fq, orc, mode, A, afmt, B, bfmt, deqA, deqB, M, N, K, seed, label):
+    pairs = sample_pairs(M, N, 2048, seed)
+    rows = np.unique(pairs[:, 0])
+    cols = np.unique(pairs[:, 1])
+    Ad = deqA(rows)
+    Bd = deqB(cols)
+    ri = np.searchsorted(rows, pairs[:, 0])
+    ci = np.searchsorted(cols, pairs[:, 1])
+    local = np.stack([ri, ci], 1).astype(np.int64)
+    Cref, D = orc.gemm_ref(Ad, Bd, local)
+    E = chunk_max_sum(Ad, Bd, local)
+    C32 = _run(fq, mode, A, afmt, B, bfmt, OUT_F32)
+    Cbf = _run(fq, mode, A, afmt, B, bfmt, OUT_BF16)
+    c32 = host(C32)[pairs[:, 0], pairs[:, 1]]
+    cbf = host(Cbf)[pairs[:, 0], pairs[:, 1]]
+    return check_gemm(c32, cbf, Cref, D, E, K, label)
+
+
+def _rows_deq(orc, mode, hq, hs, hg, fmt, block):
+    """Dequantize a subset of rows: block scales are expanded per row first."""
+    def f(rows):
+        q = np.ascontiguousarray(hq[rows])
+        if mode == BLOCK:
+            s = np.ascontiguousarray(hs[rows // block[0]])
+            return orc.dequantize(BLOCK, q, fmt, s, None, block=(1, block[1]))
+        if mode in (MX, MOSS):
+            return orc.dequantize(mode, q, fmt, np.ascontiguousarray(hs[rows]), hg)
+        return orc.dequantize(TENSOR, q, fmt, None, hg)
+    return f
+
+
+def test_gemm_fine_grained_full_size_sampled(fq, orc):
+    X, W = workloads.fine_grained_inputs()
+    A, (hqa, hsa, _) = _quant_operand(fq, orc, X, BLOCK, E4M3, (1, 128))
+    B, (hqb, hsb, _) = _quant_operand(fq, orc, W, BLOCK, E4M3, (128, 128))
+    _sampled_check(fq, orc, BLOCK, A, E4M3, B, E4M3, _rows_deq(orc, BLOCK, hqa, hsa, None, E4M3, (1, 128)),
+                   _rows_deq(orc, BLOCK, hqb, hsb, None, E4M3, (128, 128)), 4096, 2048, 7168, 3, "fine-grained")
+
+
+def test_gemm_mx_full_size_sampled(fq, orc):
+    Araw, Braw = workloads.mx_inputs()
+    A, (hqa, hsa, _) = _quant_operand(fq, orc, Araw, MX, E4M3, None)
+    B, (hqb, hsb, _) = _quant_operand(fq, orc, Braw, MX, E4M3, None)
+    _sampled_check(fq, orc, MX, A, E4M3, B, E4M3, _rows_deq(orc, MX, hqa, hsa, None, E4M3, None),
+                   _rows_deq(orc, MX, hqb, hsb, None, E4M3, None), 8192, 8192, 8192, 4, "mx 8192^3")
+
+
+def test_gemm_moss_forward_backward_full_size_sampled(fq, orc):
+    X, W, dY = workloads.moss_inputs()
+    Xq, (hx, hxs, hxg) = _quant_operand(fq, orc, X, MOSS, E4M3, None)
+    Wq, (hw, hws, hwg) = _quant_operand(fq, orc, W, MOSS, E4M3, None)
+    Gq, (hg_, hgs, hgg) = _quant_operand(fq, orc, dY, MOSS, E5M2, None)
+    XTq, (hxt, hxts, _) = _quant_operand(fq, orc, X, MOSS, E4M3, None, transpose=True, S=Xq[2])
+    WTq, (hwt, hwts, _) = _quant_operand(fq, orc, W, MOSS, E4M3, None, transpose=True, S=Wq[2])
+    GTq, (hgt, hgts, _) = _quant_operand(fq, orc, dY, MOSS, E5M2, None, transpose=True, S=Gq[2])
+    d = lambda hq, hs, hg, fmt: _rows_deq(orc, MOSS, hq, hs, hg, fmt, None)
+    # Y = X W^T
+    _sampled_check(fq, orc, MOSS, Xq, E4M3, Wq, E4M3, d(hx, hxs, hxg, E4M3), d(hw, hws, hwg, E4M3),
+                   16384, 4096, 4096, 51, "moss Y")
+    # dX = dY W  (B = W^T, grouped along out)
+    _sampled_check(fq, orc, MOSS, Gq, E5M2, WTq, E4M3, d(hg_, hgs, hgg, E5M2), d(hwt, hwts, hwg, E4M3),
+                   16384, 4096, 4096, 52, "moss dX")
+    # dW = dY^T X  (A = dY^T, B = X^T, grouped along tokens)
+    _sampled_check(fq, orc, MOSS, GTq, E5M2, XTq, E4M3, d(hgt, hgts, hgg, E5M2), d(hxt, hxts, hxg, E4M3),
+                   4096, 4096, 16384, 53, "moss dW")
+
+
+def test_gemm_determinism_and_k_zero(fq, orc):
+    xa = workloads.random_matrix(1, 256, 512)
+    xb = workloads.random_matrix(2, 192, 512)
+    A, _ = _quant_operand(fq, orc, xa, MX, E4M3, None)
+    B, _ = _quant_operand(fq, orc, xb, MX, E4M3, None)
+    c1 = host(_run(fq, MX, A, E4M3, B, E4M3, OUT_F32))
+    c2 = host(_run(fq, MX, A, E4M3, B, E4M3, OUT_F32))
+    assert np.array_equal(c1, c2)
+    z = fq.scaled_gemm(TENSOR, torch.zeros((8, 0), dtype=torch.uint8, device=DEV), E4M3, None,
+                       torch.zeros((16, 0), dtype=torch.uint8, device=DEV), E4M3, None,
+                       torch.ones(1, device=DEV), torch.ones(1, device=DEV), out_dtype=OUT_F32)
+    assert np.all(host(z) == 0.0)
