@@ -1,0 +1,280 @@
+"""Benchmark of the FP8 quantize-then-scaled-GEMM hot path on one MI355X.
+
+One step runs every scaling scheme's full path on its workload, with all inputs resident in HBM:
+  per-tensor current   A 16x32, B 32x64 fp32: amax + cast (B transposed), GEMM, fp32 out
+  delayed              one of 16 steps of A 1024x2048, B 2048x1024 bf16: casts with fused amax,
+                       GEMM (bf16 out), then both amax-history updates
+  fine-grained         X 4096x7168 (1x128) and W 2048x7168 (128x128) casts, block-scaled GEMM
+  MXFP8                A, B 8192x8192 casts, E8M0-scaled GEMM
+  MOSS fwd+bwd         X 16384x4096, W 4096x4096 (E4M3), dY 16384x4096 (E5M2): six casts
+                       (each tensor along both axes), Y = X W^T, dX = dY W, dW = dY^T X
+The headline value is the step's total GEMM flops (2 M N K per GEMM) divided by the step time,
+i.e. scaled-GEMM TFLOP/s including every quantization the path performs.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_FP8_TFLOPS = 5033.0      # MI355X dense FP8 MFMA (256 CU x 8192 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+MOSS_ELEMS = 2 * 16384 * 4096 + 4096 * 4096   # X, dY and W elements
+METRIC = "scaled FP8 GEMM TFLOP/s incl. quantize (% FP8 MFMA peak); quantize GB/s"
+WORKLOAD = ("all five scaling schemes per step: per-tensor current 16x32x64 fp32, delayed 1024x2048x1024 "
+            "bf16, fine-grained 1x128/128x128 4096x7168x2048, MXFP8 8192^3, MOSS fwd+bwd 16384x4096x4096")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP events recorded on the stream the library launches on (torch's current stream)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.events = {}     # name -> list of (start, end)
+        self.enabled = False
+
+    def __call__(self, name, fn):
+        if not self.enabled:
+            fn()
+            return
+        s = self.torch.cuda.Event(enable_timing=True)
+        e = self.torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.events.setdefault(name, []).append((s, e))
+
+    def mean_ms(self, name):
+        ev = self.events.get(name, [])
+        return sum(s.elapsed_time(e) for s, e in ev) / max(len(ev), 1)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp8_scaled_quantization_amd as fq
+    from fp8_scaled_quantization_amd import workloads as wl
+
+    fq.init()
+    dev = "cuda:0"
+    E4M3, E5M2 = fq.E4M3, fq.E5M2
+    TENSOR, BLOCK, MX, MOSS = fq.TENSOR, fq.BLOCK, fq.MX, fq.MOSS
+
+    def dbf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def zeros(shape, dt):
+        return torch.zeros(shape, dtype=dt, device=dev)
+
+    u8, f32, bf16 = torch.uint8, torch.float32, torch.bfloat16
+    t0 = time.time()
+    # ---------------- inputs (seeded, synthetic), resident in HBM
+    a1, b1 = wl.per_tensor_inputs()
+    w1 = dict(A=torch.from_numpy(a1).to(dev), B=torch.from_numpy(b1).to(dev))
+    w2 = dict(A=[], B=[])
+    for t in range(16):
+        A, B, _ = wl.delayed_inputs(t)
+        w2["A"].append(dbf16(A))
+        w2["B"].append(dbf16(B))
+    X3, W3 = wl.fine_grained_inputs()
+    w3 = dict(X=dbf16(X3), W=dbf16(W3))
+    A4, B4 = wl.mx_inputs()
+    w4 = dict(A=dbf16(A4), B=dbf16(B4))
+    X5, W5, G5 = wl.moss_inputs()
+    w5 = dict(X=dbf16(X5), W=dbf16(W5), G=dbf16(G5))
+    host_inputs = dict(a1=a1, b1=b1, X3=X3, W3=W3, A4=A4, B4=B4, X5=X5, W5=W5, G5=G5)
+    gen_s = time.time() - t0
+
+    # ---------------- outputs and state, allocated once (the library never allocates)
+    o = {}
+    o["q1a"], o["q1b"] = zeros((16, 32), u8), zeros((64, 32), u8)
+    o["s1a"], o["s1b"], o["m1a"], o["m1b"] = (zeros(1, f32) for _ in range(4))
+    o["C1"] = zeros((16, 64), f32)
+    o["q2a"], o["q2b"] = zeros((1024, 2048), u8), zeros((1024, 2048), u8)
+    o["s2a"], o["s2b"] = torch.ones(1, dtype=f32, device=dev), torch.ones(1, dtype=f32, device=dev)
+    o["h2a"], o["h2b"] = zeros(1024, f32), zeros(1024, f32)
+    o["m2a"], o["m2b"] = zeros(1, f32), zeros(1, f32)
+    o["C2"] = zeros((1024, 1024), bf16)
+    o["q3x"], o["s3x"] = zeros((4096, 7168), u8), zeros((4096, 56), f32)
+    o["q3w"], o["s3w"] = zeros((2048, 7168), u8), zeros((16, 56), f32)
+    o["C3"] = zeros((4096, 2048), bf16)
+    o["q4a"], o["e4a"] = zeros((8192, 8192), u8), zeros((8192, 256), u8)
+    o["q4b"], o["e4b"] = zeros((8192, 8192), u8), zeros((8192, 256), u8)
+    o["C4"] = zeros((8192, 8192), bf16)
+    for n, (r, c) in dict(X=(16384, 4096), W=(4096, 4096), G=(16384, 4096)).items():
+        o["q5" + n], o["e5" + n] = zeros((r, c), u8), zeros((r, c // 32), u8)
+        o["q5" + n + "T"], o["e5" + n + "T"] = zeros((c, r), u8), zeros((c, r // 32), u8)
+        o["S5" + n], o["m5" + n] = zeros(1, f32), zeros(1, f32)
+    o["Y5"], o["dX5"], o["dW5"] = zeros((16384, 4096), bf16), zeros((16384, 4096), bf16), zeros((4096, 4096), bf16)
+
+    timer = Timer(torch)
+    Q, G_ = fq.fp8_quantize, fq.fp8_scaled_gemm
+
+    def step(i):
+        # per-tensor current scaling
+        timer("q1", lambda: (Q(TENSOR, E4M3, w1["A"], o["q1a"], None, o["s1a"], False, o["m1a"]),
+                             Q(TENSOR, E4M3, w1["B"], o["q1b"], None, o["s1b"], False, o["m1b"], transpose_out=True)))
+        timer("g1", lambda: G_(TENSOR, o["q1a"], E4M3, None, o["q1b"], E4M3, None, o["s1a"], o["s1b"], o["C1"], fq.OUT_F32))
+        # delayed scaling: casts with the state's scales (fused amax), GEMM, then history updates
+        t = i % 16
+        timer("q2", lambda: (Q(TENSOR, E4M3, w2["A"][t], o["q2a"], None, o["s2a"], True, o["m2a"]),
+                             Q(TENSOR, E4M3, w2["B"][t], o["q2b"], None, o["s2b"], True, o["m2b"], transpose_out=True)))
+        timer("g2", lambda: G_(TENSOR, o["q2a"], E4M3, None, o["q2b"], E4M3, None, o["s2a"], o["s2b"], o["C2"], fq.OUT_BF16))
+        timer("h2", lambda: (fq.fp8_history_update(o["h2a"], o["m2a"], o["s2a"], E4M3),
+                             fq.fp8_history_update(o["h2b"], o["m2b"], o["s2b"], E4M3)))
+        # fine-grained block scaling
+        timer("q3x", lambda: Q(BLOCK, E4M3, w3["X"], o["q3x"], o["s3x"], block=(1, 128)))
+        timer("q3w", lambda: Q(BLOCK, E4M3, w3["W"], o["q3w"], o["s3w"], block=(128, 128)))
+        timer("g3", lambda: G_(BLOCK, o["q3x"], E4M3, o["s3x"], o["q3w"], E4M3, o["s3w"], None, None, o["C3"], fq.OUT_BF16))
+        # MXFP8
+        timer("q4", lambda: (Q(MX, E4M3, w4["A"], o["q4a"], o["e4a"]), Q(MX, E4M3, w4["B"], o["q4b"], o["e4b"])))
+        timer("g4", lambda: G_(MX, o["q4a"], E4M3, o["e4a"], o["q4b"], E4M3, o["e4b"], None, None, o["C4"], fq.OUT_BF16))
+        # MOSS forward + backward
+        for n, fmt in (("X", E4M3), ("W", E4M3), ("G", E5M2)):
+            timer("q5", lambda: Q(MOSS, fmt, w5[n], o["q5" + n], o["e5" + n], o["S5" + n], False, o["m5" + n]))
+            timer("q5T", lambda: Q(MOSS, fmt, w5[n], o["q5" + n + "T"], o["e5" + n + "T"], o["S5" + n], True,
+                                   transpose_out=True))
+        timer("g5", lambda: G_(MOSS, o["q5X"], E4M3, o["e5X"], o["q5W"], E4M3, o["e5W"], o["S5X"], o["S5W"], o["Y5"], fq.OUT_BF16))
+        timer("g5", lambda: G_(MOSS, o["q5G"], E5M2, o["e5G"], o["q5WT"], E4M3, o["e5WT"], o["S5G"], o["S5W"], o["dX5"], fq.OUT_BF16))
+        timer("g5", lambda: G_(MOSS, o["q5GT"], E5M2, o["e5GT"], o["q5XT"], E4M3, o["e5XT"], o["S5G"], o["S5X"], o["dW5"], fq.OUT_BF16))
+
+    # ---------------- flops and algorithmic bytes
+    gemm_flops = {"g1": 2 * 16 * 64 * 32, "g2": 2 * 1024 * 1024 * 2048, "g3": 2 * 4096 * 2048 * 7168,
+                  "g4": 2 * 8192 ** 3, "g5": 2 * 16384 * 4096 * 4096}            # g5: per launch
+    launches = {"g1": 1, "g2": 1, "g3": 1, "g4": 1, "g5": 3}
+    step_flops = sum(gemm_flops[k] * launches[k] for k in gemm_flops)
+    # bytes per quantize call: input read (+ the amax pass's read when the scale is derived),
+    # FP8 write, scale write
+    qbytes = {
+        "q1": (16 * 32 + 32 * 64) * 4 * 2 + (16 * 32 + 32 * 64),
+        "q2": 2 * (1024 * 2048 * 3),
+        "q3x": 4096 * 7168 * 3 + 4096 * 56 * 4,
+        "q3w": 2048 * 7168 * 3 + 16 * 56 * 4,
+        "q4": 2 * (8192 * 8192 * 3 + 8192 * 256),
+        "q5": MOSS_ELEMS * (2 + 2 + 1) + MOSS_ELEMS // 32,
+        "q5T": MOSS_ELEMS * (2 + 1) + MOSS_ELEMS // 32,
+    }
+    qcalls = {"q1": 1, "q2": 1, "q3x": 1, "q3w": 1, "q4": 1, "q5": 3, "q5T": 3}
+
+    # ---------------- warmup, then the timed steps
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    timer.enabled = True
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    tflops = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    per = {}
+    for k in gemm_flops:
+        ms = timer.mean_ms(k)
+        per[k] = dict(ms=round(ms, 5), tflops=round(gemm_flops[k] / (ms * 1e-3) / 1e12, 2),
+                      pct_fp8_peak=round(100 * gemm_flops[k] / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 2))
+    for k in qbytes:
+        ms = timer.mean_ms(k)
+        per_call = qbytes[k] / qcalls[k]
+        per[k] = dict(ms=round(ms, 5), gbs=round(per_call / (ms * 1e-3) / 1e9, 1),
+                      pct_hbm_peak=round(100 * per_call / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2))
+    per["h2"] = dict(ms=round(timer.mean_ms("h2"), 5))
+    quant_ms = sum(timer.mean_ms(k) * qcalls[k] for k in qbytes)
+    quant_gbs = sum(qbytes.values()) / (quant_ms * 1e-3) / 1e9
+    # dominant kernel: the GEMM launch with the largest total time per step
+    dom = max(gemm_flops, key=lambda k: timer.mean_ms(k) * launches[k])
+    dom_ms = timer.mean_ms(dom)
+    dom_tf = gemm_flops[dom] / (dom_ms * 1e-3) / 1e12
+    names = {"g1": "per-tensor GEMM 16x64x32", "g2": "delayed GEMM 1024x1024x2048", "g3": "block GEMM 4096x2048x7168",
+             "g4": "MX GEMM 8192x8192x8192", "g5": "MOSS GEMM 16384x4096x4096 (avg of Y, dX, dW)"}
+    roofline = {"kernel": names[dom], "bound": "mfma", "achieved": round(dom_tf, 2), "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                "avg_launch_ms": round(dom_ms, 5)}
+
+    out = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8 e4m3/e5m2 operands, fp32 accumulate", "data": "synthetic (seeded numpy PCG64)",
+        "config": {"workload": WORKLOAD, "gemm_tflop_per_step": round(step_flops / 1e12, 4), "parallelism": "single GPU"},
+        "pct_fp8_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
+        "quantize_gbs": round(quant_gbs, 1), "quantize_pct_hbm_peak": round(100 * quant_gbs / PEAK_HBM_GBS, 2),
+        "roofline": roofline, "per_kernel": per, "input_gen_s": round(gen_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(host_inputs)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(h):
+    """The CPU oracle timed on a bounded sample of the same step: every workload's quantization of a
+    row sample (all rows for the small workloads) and its fp64 GEMM for a sample of output rows
+    and columns; throughput in the metric's unit (GEMM TFLOP/s incl. quantize)."""
+    import oracle.oracle as orc
+    lib = orc.lib()   # noqa: F841  (loads and, if needed, builds the oracle)
+    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    flops = 0.0
+    t0 = time.time()
+    # per-tensor current, whole workload
+    qa, sa = orc.quantize_tensor_current(h["a1"], 0)
+    qb, sb = orc.quantize_tensor_current(h["b1"], 0, transpose=True)
+    orc.gemm_ref(orc.dequantize(0, qa, 0, None, sa), orc.dequantize(0, qb, 0, None, sb))
+    flops += 2 * 16 * 64 * 32
+    r = 1280  # sampled rows of each operand for the large workloads
+    # fine-grained: r rows of X and one 128-row block of W, GEMM r x 128 x 7168
+    qx, sx = orc.quantize_block(np.ascontiguousarray(h["X3"][:r]), 0, 1, 128)
+    qw, sw = orc.quantize_block(np.ascontiguousarray(h["W3"][:128]), 0, 128, 128)
+    orc.gemm_ref(orc.dequantize(1, qx, 0, sx, None, block=(1, 128)), orc.dequantize(1, qw, 0, sw, None, block=(128, 128)))
+    flops += 2 * r * 128 * 7168
+    # MX: r rows of A and B, GEMM r x r x 8192
+    qa, ea = orc.quantize_mx(np.ascontiguousarray(h["A4"][:r]), 0)
+    qb, eb = orc.quantize_mx(np.ascontiguousarray(h["B4"][:r]), 0)
+    orc.gemm_ref(orc.dequantize(2, qa, 0, ea), orc.dequantize(2, qb, 0, eb))
+    flops += 2 * r * r * 8192
+    # MOSS: global factors over the whole tensors, then r-row samples of each copy and the 3 GEMMs
+    S = {n: orc.compute_scale(orc.amax(h[k]), f, 1.0) for n, k, f in (("X", "X5", 0), ("W", "W5", 0), ("G", "G5", 1))}
+    qX, eX = orc.quantize_moss_given(np.ascontiguousarray(h["X5"][:r]), 0, S["X"])
+    qW, eW = orc.quantize_moss_given(np.ascontiguousarray(h["W5"][:r]), 0, S["W"])
+    qG, eG = orc.quantize_moss_given(np.ascontiguousarray(h["G5"][:r]), 1, S["G"])
+    qWT, eWT = orc.quantize_moss_given(np.ascontiguousarray(h["W5"][:, :r]), 0, S["W"], transpose=True)
+    qGT, eGT = orc.quantize_moss_given(np.ascontiguousarray(h["G5"][:, :r]), 1, S["G"], transpose=True)
+    qXT, eXT = orc.quantize_moss_given(np.ascontiguousarray(h["X5"][:, :r]), 0, S["X"], transpose=True)
+    d = lambda q, e, f, s: orc.dequantize(3, q, f, e, s)
+    orc.gemm_ref(d(qX, eX, 0, S["X"]), d(qW, eW, 0, S["W"]))
+    orc.gemm_ref(d(qG, eG, 1, S["G"]), d(qWT, eWT, 0, S["W"]))
+    orc.gemm_ref(d(qGT, eGT, 1, S["G"]), d(qXT, eXT, 0, S["X"]))
+    flops += 2 * r * r * 4096 * 2 + 2 * r * r * 16384
+    secs = time.time() - t0
+    return {"value": round(flops / secs / 1e12, 8), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": round(secs, 2),
+            "sample": ("oracle quantize + fp64 GEMM: whole per-tensor workload; 1280-row samples of the fine-grained "
+                       "(x one 128-row weight block), MX and all six MOSS copies (global factors over whole "
+                       "tensors), GEMMs over those rows/columns; delayed workload not sampled")}
+
+
+if __name__ == "__main__":
+    main()
