@@ -2,16 +2,19 @@
 dequantization of row samples, and the GEMM error bound.
 
 GEMM tolerance.  The oracle's reference is the exact (fp64) product of the dequantized operands.
-The library reduces each 128-wide K chunk with gfx950's FP8 matrix instruction and adds the FP32
-result into an FP32 accumulator.  Measured on the hardware, one such instruction's result differs
-from the exact sum of its products by at most 2^-11.1 times the largest product magnitude in the
-chunk (over 2048 x 256 random chunks, with and without outliers and scales); FP32 accumulation,
-the block-scale product fl(sx*sw) and the epilogue factor each add at most one unit roundoff
-(2^-24) of D = sum_k |a_k b_k| per operation.  The elementwise bound used in the tests is therefore
-    |C - C_ref| <= 2^-10 * E + (K/128 + 3) * 2^-24 * D,
-with E = sum over 128-wide K chunks of max_k |a_k b_k| (a factor-2 margin on the measured 2^-11.1).
-The bf16 output must equal round-to-nearest-even of the same kernel's fp32 output bit for bit, and
-its normwise relative error must stay within 2e-3.
+The library reduces K in 128-wide steps with gfx950's FP8 matrix instruction.  Measured on the
+hardware, one such instruction adds its 128 products with an error of at most 2^-11.1 times the
+largest product magnitude (over 2048 x 256 random steps, with and without outliers and scales),
+and adds its C input with an error of at most 2^-15.2 times |C| (inputs up to 10^4 times the
+products).  BLOCK scaling promotes every step into an FP32 accumulator (one more rounding of
+2^-24 |acc| per step, plus the rounding of the block-scale product fl(sx*sw)); the other schemes
+keep the whole K sum in the instruction's accumulator, so step k also carries the C-input error
+of the running sum S_{k-1}.  The elementwise bound used in the tests is therefore
+    |C - C_ref| <= 2^-10 * E + 2^-13 * Sigma + (K/128 + 3) * 2^-24 * D,
+with E = sum over 128-wide K steps of max_k |a_k b_k|, Sigma = sum over steps of |S_{k-1}| (exact
+prefix sums of the per-step partial products; 0 for BLOCK), D = sum_k |a_k b_k|, and margins of
+2.2x and 4.5x on the measured constants.  The bf16 output must equal round-to-nearest-even of the
+same kernel's fp32 output bit for bit, and its normwise relative error must stay within 2e-3.
 """
 from __future__ import annotations
 
@@ -89,25 +92,50 @@ def chunk_max_sum(A: np.ndarray, B: np.ndarray, pairs=None, chunk: int = 128):
     return E
 
 
-def gemm_bound(E, D, K):
-    return 2.0 ** -10 * E + (K / 128.0 + 3.0) * 2.0 ** -24 * D
+def chain_prefix_abs(A: np.ndarray, B: np.ndarray, pairs=None, chunk: int = 128):
+    """Sigma[m,n] = sum over K steps k of |S_{k-1}|, S_j = exact sum of the first j step partials."""
+    K = A.shape[1]
+    nck = -(-K // chunk)
+    pad = nck * chunk - K
+    if pad:
+        A = np.pad(A, ((0, 0), (0, pad)))
+        B = np.pad(B, ((0, 0), (0, pad)))
+    Ar = A.reshape(A.shape[0], nck, chunk)
+    Br = B.reshape(B.shape[0], nck, chunk)
+    if pairs is not None:
+        P = np.einsum("pkc,pkc->pk", Ar[pairs[:, 0]], Br[pairs[:, 1]])
+    else:
+        P = np.einsum("mkc,nkc->mnk", Ar, Br)
+    S = np.cumsum(P, axis=-1) - P
+    return np.abs(S).sum(axis=-1)
+
+
+def gemm_bound(E, D, K, Sigma=None):
+    b = 2.0 ** -10 * E + (K / 128.0 + 3.0) * 2.0 ** -24 * D
+    if Sigma is not None:
+        b = b + 2.0 ** -13 * Sigma
+    return b
 
 
 def check_gemm(C32: np.ndarray, Cbf: np.ndarray | None, Cref: np.ndarray, D: np.ndarray, E: np.ndarray, K: int,
-               label: str = ""):
+               label: str = "", Sigma=None):
     """Assert the elementwise bound on the fp32 output, bf16 == RNE(fp32), normwise bf16 error."""
     err = np.abs(C32.astype(np.float64) - Cref)
-    bound = gemm_bound(E, D, K)
+    bound = gemm_bound(E, D, K, Sigma)
     bad = err > bound
+    worst = float((err / np.maximum(bound, 1e-300)).max()) if err.size else 0.0
+    print("%s: worst err/bound %.3g, max err/D %.3g" % (label, worst, float((err / np.maximum(D, 1e-300)).max()) if err.size else 0.0))
     assert not bad.any(), "%s: %d of %d outputs exceed the bound; worst err/bound %.3g" % (
-        label, int(bad.sum()), bad.size, float((err / np.maximum(bound, 1e-300)).max()))
+        label, int(bad.sum()), bad.size, worst)
     if Cbf is not None:
         assert np.array_equal(Cbf, bf16_rne_bits(C32)), "%s: bf16 output is not RNE(fp32 output)" % label
         cb = workloads.bf16_bits_to_f32(Cbf).astype(np.float64)
         nrm = np.linalg.norm(Cref)
         if nrm > 0:
-            assert np.linalg.norm(cb - Cref) / nrm <= 2e-3, label
-    return float((err / np.maximum(bound, 1e-300)).max())
+            rel = np.linalg.norm(cb - Cref) / nrm
+            print("%s: bf16 normwise relative error %.3g" % (label, rel))
+            assert rel <= 2e-3, label
+    return worst
 
 
 def sample_pairs(M: int, N: int, n: int, seed: int, tile: int = 128) -> np.ndarray:

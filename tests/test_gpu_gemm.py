@@ -7,7 +7,7 @@ import pytest
 import torch
 
 from fp8_scaled_quantization_amd import workloads
-from tests.gpu_util import DEV, check_gemm, chunk_max_sum, host, sample_pairs, to_dev
+from tests.gpu_util import DEV, chain_prefix_abs, check_gemm, chunk_max_sum, host, sample_pairs, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -65,9 +65,10 @@ def test_gemm_small_full(fq, orc, mode, M, N, K, fmts):
     Bd = _deq(orc, mode, hqb, hsb, hgb, bfmt, bb)
     Cref, D = orc.gemm_ref(Ad, Bd)
     E = chunk_max_sum(Ad, Bd)
+    Sg = None if mode == BLOCK else chain_prefix_abs(Ad, Bd)
     C32 = host(_run(fq, mode, A, afmt, B, bfmt, OUT_F32))
     Cbf = host(_run(fq, mode, A, afmt, B, bfmt, OUT_BF16))
-    check_gemm(C32, Cbf, Cref, D, E, K, "mode %d %dx%dx%d" % (mode, M, N, K))
+    check_gemm(C32, Cbf, Cref, D, E, K, "mode %d %dx%dx%d" % (mode, M, N, K), Sg)
 
 
 def test_gemm_per_tensor_small_exact_config(fq, orc):
@@ -80,7 +81,7 @@ def test_gemm_per_tensor_small_exact_config(fq, orc):
     Bd = orc.dequantize(TENSOR, hqb, E4M3, None, hgb)
     Cref, D = orc.gemm_ref(Ad, Bd)
     C32 = host(_run(fq, TENSOR, A, E4M3, B, E4M3, OUT_F32))
-    worst = check_gemm(C32, None, Cref, D, chunk_max_sum(Ad, Bd), 32, "16x32x64")
+    worst = check_gemm(C32, None, Cref, D, chunk_max_sum(Ad, Bd), 32, "16x32x64", chain_prefix_abs(Ad, Bd))
     assert np.allclose(D, np.abs(Cref))
     assert np.max(np.abs(C32 - Cref) / np.abs(Cref)) < 1e-3 and worst <= 1.0
 
@@ -96,7 +97,7 @@ def test_gemm_delayed_step_full(fq, orc):
     E = chunk_max_sum(Ad, Bd)
     C32 = host(_run(fq, TENSOR, A, E4M3, B, E4M3, OUT_F32))
     Cbf = host(_run(fq, TENSOR, A, E4M3, B, E4M3, OUT_BF16))
-    check_gemm(C32, Cbf, Cref, D, E, 2048, "delayed 1024x1024x2048")
+    check_gemm(C32, Cbf, Cref, D, E, 2048, "delayed 1024x1024x2048", chain_prefix_abs(Ad, Bd))
 
 
 def _sampled_check(fq, orc, mode, A, afmt, B, bfmt, deqA, deqB, M, N, K, seed, label):
@@ -110,11 +111,12 @@ def _sampled_check(fq, orc, mode, A, afmt, B, bfmt, deqA, deqB, M, N, K, seed, l
     local = np.stack([ri, ci], 1).astype(np.int64)
     Cref, D = orc.gemm_ref(Ad, Bd, local)
     E = chunk_max_sum(Ad, Bd, local)
+    Sg = None if mode == BLOCK else chain_prefix_abs(Ad, Bd, local)
     C32 = _run(fq, mode, A, afmt, B, bfmt, OUT_F32)
     Cbf = _run(fq, mode, A, afmt, B, bfmt, OUT_BF16)
     c32 = host(C32)[pairs[:, 0], pairs[:, 1]]
     cbf = host(Cbf)[pairs[:, 0], pairs[:, 1]]
-    return check_gemm(c32, cbf, Cref, D, E, K, label)
+    return check_gemm(c32, cbf, Cref, D, E, K, label, Sg)
 
 
 def _rows_deq(orc, mode, hq, hs, hg, fmt, block):
