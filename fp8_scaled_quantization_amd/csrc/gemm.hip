@@ -243,11 +243,11 @@ static void launch_t(const GemmArgs& g, hipStream_t st) {
 
 // Pipelined kernels (gemm_kernel.cuh) for K % 128 == 0 and operands addressable with 32-bit
 // buffer offsets; the reference-tile kernel above handles everything else (ragged K, huge operands).
-template <int MODE, int AFMT, int BFMT, bool OUT, int BM_, int BN_, int WM, int WN, int R, int S>
+template <int MODE, int AFMT, int BFMT, bool OUT, int BM_, int BN_, int WM, int WN, int S>
 static void launch_v2(const GemmArgs& g, hipStream_t st) {
     const int64_t ntm = (g.M + BM_ - 1) / BM_, ntn = (g.N + BN_ - 1) / BN_;
-    auto kern = g2::gemm_kernel<MODE, AFMT, BFMT, OUT, BM_, BN_, WM, WN, R, S>;
-    constexpr size_t smem = g2::smem_bytes<BM_, BN_, S>();
+    auto kern = g2::gemm_kernel<MODE, AFMT, BFMT, OUT, BM_, BN_, WM, WN, S>;
+    constexpr size_t smem = g2::smem_bytes<MODE, BM_, BN_, S>();
     static bool attr_set = false;
     if (!attr_set) {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
@@ -268,13 +268,13 @@ static void launch_sel(const GemmArgs& g, hipStream_t st) {
     }
     if constexpr (MODE == kModeBlock) {
         // per-128 promotion with the block scales: 256 x 128 tiles, 8 waves of 64 x 64
-        launch_v2<MODE, AFMT, BFMT, OUT, 256, 128, 4, 2, 1, 3>(g, st);
+        launch_v2<MODE, AFMT, BFMT, OUT, 256, 128, 4, 2, 3>(g, st);
     } else {
         // whole-K accumulation on the matrix cores: 256 x 256 tiles, 8 waves of 64 x 128, when
         // there are enough tiles to fill the GPU; 128 x 128 tiles otherwise
         const int64_t big_tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256);
-        if (big_tiles >= 192) launch_v2<MODE, AFMT, BFMT, OUT, 256, 256, 4, 2, 0, 2>(g, st);
-        else launch_v2<MODE, AFMT, BFMT, OUT, 128, 128, 2, 2, 0, 3>(g, st);
+        if (big_tiles >= 192) launch_v2<MODE, AFMT, BFMT, OUT, 256, 256, 4, 2, 2>(g, st);
+        else launch_v2<MODE, AFMT, BFMT, OUT, 128, 128, 2, 2, 3>(g, st);
     }
 }
 
