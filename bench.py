@@ -38,7 +38,43 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run one plain 256 MiB device copy (read + write) whose "
+                         "known size calibrates the HBM byte counters of a profiler run")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "gemm_moss_16384x4096x4096_hbm_traffic.md")
+GEMM_SOURCES = ("fp8_scaled_quantization_amd/csrc/gemm_kernel.cuh", "fp8_scaled_quantization_amd/csrc/gemm.hip",
+                "fp8_scaled_quantization_amd/csrc/kernels.h", "fp8_scaled_quantization_amd/csrc/common.cuh")
+
+
+def gemm_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the MOSS GEMM from the committed counter summary, or None when that
+    summary is missing or was taken on GEMM sources other than the ones in this tree."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            txt = f.read()
+    except OSError:
+        return None
+    fields = dict(line.split(":", 1) for line in txt.splitlines() if line.startswith(("source_sha256:", "bytes_per_launch:")))
+    if fields.get("source_sha256", "").strip() != gemm_source_digest():
+        return None
+    try:
+        return int(fields["bytes_per_launch"].strip())
+    except (KeyError, ValueError):
+        return None
 
 
 class Timer:
@@ -213,8 +249,16 @@ def main():
     names = {"g1": "per-tensor GEMM 16x64x32", "g2": "delayed GEMM 1024x1024x2048", "g3": "block GEMM 4096x2048x7168",
              "g4": "MX GEMM 8192x8192x8192", "g5": "MOSS GEMM 16384x4096x4096 (avg of Y, dX, dW)"}
     roofline = {"kernel": names[dom], "bound": "mfma", "achieved": round(dom_tf, 2), "peak": PEAK_FP8_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_FP8_TFLOPS, 4),
+                "traffic": measured_traffic() if dom == "g5" else None, "traffic_unit": "bytes per launch",
                 "avg_launch_ms": round(dom_ms, 5)}
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)          # 256 MiB read + 256 MiB written
+        torch.cuda.synchronize()
+        del src, dst
 
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -244,7 +288,7 @@ def cpu_baseline(h):
     qb, sb = orc.quantize_tensor_current(h["b1"], 0, transpose=True)
     orc.gemm_ref(orc.dequantize(0, qa, 0, None, sa), orc.dequantize(0, qb, 0, None, sb))
     flops += 2 * 16 * 64 * 32
-    r = 1280  # sampled rows of each operand for the large workloads
+    r = 2048  # sampled rows of each operand for the large workloads
     # fine-grained: r rows of X and one 128-row block of W, GEMM r x 128 x 7168
     qx, sx = orc.quantize_block(np.ascontiguousarray(h["X3"][:r]), 0, 1, 128)
     qw, sw = orc.quantize_block(np.ascontiguousarray(h["W3"][:128]), 0, 128, 128)
@@ -271,7 +315,7 @@ def cpu_baseline(h):
     secs = time.time() - t0
     return {"value": round(flops / secs / 1e12, 8), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "seconds": round(secs, 2),
-            "sample": ("oracle quantize + fp64 GEMM: whole per-tensor workload; 1280-row samples of the fine-grained "
+            "sample": ("oracle quantize + fp64 GEMM: whole per-tensor workload; 2048-row samples of the fine-grained "
                        "(x one 128-row weight block), MX and all six MOSS copies (global factors over whole "
                        "tensors), GEMMs over those rows/columns; delayed workload not sampled")}
 
