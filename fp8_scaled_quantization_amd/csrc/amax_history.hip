@@ -4,7 +4,7 @@
 // fp32 bit patterns as unsigned integers: for non-negative floats integer order is numeric order and
 // every NaN pattern sorts above +Inf, so the result is exact, NaN-propagating and independent of the
 // order in which workgroups finish.  Each workgroup reduces in registers and LDS and issues one
-// global atomic max.
+// global atomic max into the output, which a one-thread kernel zeroes first.
 #include "common.cuh"
 #include "kernels.h"
 
@@ -14,45 +14,100 @@ namespace fp8q {
 
 __global__ void fill_u32_kernel(uint32_t* p, uint32_t v) { *p = v; }
 
-// Grid-stride amax over rows x cols (leading dimension ld).  Each thread handles 8 consecutive
-// elements per step; cols % 8 == 0 and 16-byte aligned rows are guaranteed by the host.
+// Same-address atomics serialize in L2 (on the order of 10 ns each), so the reductions below use at
+// most kAmaxBlocks workgroups of 1024 threads, each issuing one atomic max.
+constexpr int kAmaxThreads = 1024;
+constexpr int64_t kAmaxBlocks = 256;
+constexpr int kAmaxUnroll = 8;       // 16-byte loads in flight per thread
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Running max of |x| over one 16-byte vector.  bf16: the sign-cleared 16-bit patterns are kept as
+// two packed unsigned maxima (bf16 is the upper half of fp32, so the same integer order holds);
+// fp32: the sign-cleared 32-bit patterns.
 template <bool BF16>
-__global__ __launch_bounds__(256) void amax_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
-                                                   int64_t ld, uint32_t* __restrict__ out) {
-    const int64_t chunks_per_row = cols / 8;
-    const int64_t total = rows * chunks_per_row;
-    const size_t esz = BF16 ? 2 : 4;
-    uint32_t m = 0;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-        int64_t r = i / chunks_per_row, c = (i - r * chunks_per_row) * 8;
-        float v[8];
-        load8<BF16>(static_cast<const char*>(x) + (r * ld + c) * esz, v);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) m = max(m, absbits(v[j]));
+__device__ __forceinline__ uint32_t vmax_acc(uint32_t m, uint4 w) {
+    if (BF16) {
+        u16x2 a = __builtin_bit_cast(u16x2, w.x & 0x7FFF7FFFu), b = __builtin_bit_cast(u16x2, w.y & 0x7FFF7FFFu);
+        u16x2 c = __builtin_bit_cast(u16x2, w.z & 0x7FFF7FFFu), d = __builtin_bit_cast(u16x2, w.w & 0x7FFF7FFFu);
+        u16x2 r = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+        return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, m), r));
     }
+    return max(max(m, max(w.x & 0x7FFFFFFFu, w.y & 0x7FFFFFFFu)), max(w.z & 0x7FFFFFFFu, w.w & 0x7FFFFFFFu));
+}
+
+// packed accumulator -> fp32 |x| bit pattern
+template <bool BF16>
+__device__ __forceinline__ uint32_t vmax_final(uint32_t m) {
+    return BF16 ? max(m & 0xFFFFu, m >> 16) << 16 : m;
+}
+
+__device__ __forceinline__ void block1024_atomic_max(uint32_t m, uint32_t* out) {
+    __shared__ uint32_t red[16];
     m = wave_max_u32(m);
-    __shared__ uint32_t red[4];
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t b = max(max(red[0], red[1]), max(red[2], red[3]));
-        atomicMax(out, b);
+    if (threadIdx.x < 64) {
+        uint32_t v = threadIdx.x < 16 ? red[threadIdx.x] : 0u;
+        v = wave_max_u32(v);
+        if (threadIdx.x == 0) atomicMax(out, v);
     }
+}
+
+// Contiguous tensor as nv 16-byte vectors; each thread keeps kAmaxUnroll loads in flight.
+template <bool BF16>
+__global__ __launch_bounds__(kAmaxThreads) void amax_flat_kernel(const uint4* __restrict__ x, int64_t nv,
+                                                                 uint32_t* __restrict__ out) {
+    constexpr int U = kAmaxUnroll, T = kAmaxThreads;
+    const int64_t stride = (int64_t)gridDim.x * T * U;
+    uint32_t m = 0;
+    for (int64_t b = (int64_t)blockIdx.x * T * U + threadIdx.x; b < nv; b += stride) {
+        uint4 w[U];
+        if (b + (int64_t)(U - 1) * T < nv) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) w[u] = x[b + u * T];
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u) w[u] = b + u * T < nv ? x[b + u * T] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) m = vmax_acc<BF16>(m, w[u]);
+    }
+    block1024_atomic_max(vmax_final<BF16>(m), out);
+}
+
+// Strided rows (ld > cols): workgroups stride over rows, threads over the row's 16-byte vectors.
+template <bool BF16>
+__global__ __launch_bounds__(kAmaxThreads) void amax_rows_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                                 int64_t ld, uint32_t* __restrict__ out) {
+    const size_t esz = BF16 ? 2 : 4;
+    const int64_t vpr = cols * (int64_t)esz / 16;      // cols % 8 == 0: whole vectors per row
+    uint32_t m = 0;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const uint4* row = reinterpret_cast<const uint4*>(static_cast<const char*>(x) + r * ld * (int64_t)esz);
+        for (int64_t v = threadIdx.x; v < vpr; v += kAmaxThreads) m = vmax_acc<BF16>(m, row[v]);
+    }
+    block1024_atomic_max(vmax_final<BF16>(m), out);
 }
 
 int launch_amax(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ld, float* amax_out,
                 hipStream_t st) {
-    hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(1), 0, st, reinterpret_cast<uint32_t*>(amax_out), 0u);
-    int64_t total = rows * (cols / 8);
-    if (total == 0) return 0;
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > kMaxReduceBlocks) blocks = kMaxReduceBlocks;
-    if (bf16)
-        hipLaunchKernelGGL(amax_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols, ld,
-                           reinterpret_cast<uint32_t*>(amax_out));
-    else
-        hipLaunchKernelGGL(amax_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols, ld,
-                           reinterpret_cast<uint32_t*>(amax_out));
+    uint32_t* out = reinterpret_cast<uint32_t*>(amax_out);
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(1), 0, st, out, 0u);
+    if (rows == 0 || cols == 0) return 0;
+    const size_t esz = bf16 ? 2 : 4;
+    if (ld == cols) {
+        const int64_t nv = rows * cols * (int64_t)esz / 16;
+        int64_t blocks = (nv + kAmaxThreads * kAmaxUnroll - 1) / (kAmaxThreads * kAmaxUnroll);
+        if (blocks > kAmaxBlocks) blocks = kAmaxBlocks;
+        const uint4* xv = static_cast<const uint4*>(x);
+        if (bf16) hipLaunchKernelGGL(amax_flat_kernel<true>, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, st, xv, nv, out);
+        else hipLaunchKernelGGL(amax_flat_kernel<false>, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, st, xv, nv, out);
+    } else {
+        const int64_t blocks = rows < kAmaxBlocks ? rows : kAmaxBlocks;
+        if (bf16) hipLaunchKernelGGL(amax_rows_kernel<true>, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, st, x, rows, cols, ld, out);
+        else hipLaunchKernelGGL(amax_rows_kernel<false>, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, st, x, rows, cols, ld, out);
+    }
     return 0;
 }
 

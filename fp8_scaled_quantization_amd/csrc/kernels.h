@@ -6,7 +6,7 @@
 
 namespace fp8q {
 
-constexpr int64_t kMaxReduceBlocks = 1024;   // workgroups issuing one global atomic each
+constexpr int64_t kMaxReduceBlocks = 256;    // cap on workgroups that each end with one same-address atomic
 constexpr int kModeTensor = 0, kModeBlock = 1, kModeMX = 2, kModeMoss = 3;
 
 int launch_amax(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ld, float* amax_out,
@@ -30,6 +30,7 @@ struct CastArgs {
     const float* amax_in;            // TENSOR current / MOSS: tensor amax to derive the scale from
     float* scale_out;                // written by workgroup 0 when the scale is derived here
     float* amax_out;                 // fused amax (TENSOR with a given scale), may be null
+    int tile_group;                  // transposed kernel: 128-row tile bands walked per column strip
 };
 
 // Casts with the tensor scale (or S) either given (scale_in) or derived from amax_in.

@@ -111,7 +111,8 @@ __device__ __forceinline__ UniformScale uniform_scale(const CastArgs& a) {
 
 // Process one lane chunk v[32] (all 64 lanes of the wave call this together: BLOCK uses shuffles).
 // Returns the per-lane scale value to store (BLOCK: fp32 bits; MX/MOSS: E8M0 byte) in `sc`.
-template <int FMT, int MODE>
+// BLOCK 1x128: the four chunks of a group sit in lanes l, l ^ G, l ^ 2G, l ^ 3G.
+template <int FMT, int MODE, int G = 1>
 __device__ __forceinline__ void process_chunk(const float* v, const UniformScale& u, uint32_t* out,
                                               uint32_t& sc, uint32_t& chunk_max) {
     ChunkStats st = chunk_stats(v);
@@ -119,7 +120,11 @@ __device__ __forceinline__ void process_chunk(const float* v, const UniformScale
     if (MODE == kModeTensor) {
         cast32_div<FMT, false>(v, u.s, u.y, 0, u.ok && dividends_ok(st.mx, st.mn), out);
     } else if (MODE == kModeBlock) {
-        uint32_t gmx = group_max_u32<4>(st.mx);
+        uint32_t gmx = st.mx;
+        uint32_t o = (uint32_t)__shfl_xor((int)gmx, G, 64);
+        gmx = max(gmx, o);
+        o = (uint32_t)__shfl_xor((int)gmx, 2 * G, 64);
+        gmx = max(gmx, o);
         float s = scale_from_amax<FMT>(__uint_as_float(gmx), 1.0f);
         float y = recip_rn(s);
         cast32_div<FMT, false>(v, s, y, 0, divisor_ok(s) && dividends_ok(st.mx, st.mn), out);
@@ -141,24 +146,33 @@ __device__ __forceinline__ void store32(uint8_t* p, const uint32_t* w) {
     reinterpret_cast<uint4*>(p)[1] = make_uint4(w[4], w[5], w[6], w[7]);
 }
 
+// Workgroup max, then one atomic max into *out (same-address atomics serialize in L2, so callers keep
+// the number of workgroups that do this small).
+template <int THREADS>
 __device__ __forceinline__ void block_reduce_atomic(uint32_t m, float* out) {
-    __shared__ uint32_t red[4];
+    constexpr int NW = THREADS / 64;
+    __shared__ uint32_t red[NW];
     m = wave_max_u32(m);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
-    if (threadIdx.x == 0) atomicMax(reinterpret_cast<uint32_t*>(out), max(max(red[0], red[1]), max(red[2], red[3])));
+    if (threadIdx.x == 0) {
+        uint32_t b = red[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) b = max(b, red[w]);
+        atomicMax(reinterpret_cast<uint32_t*>(out), b);
+    }
 }
 
 // ------------------------------------------------------------------ row kernel
 // Output = input layout (rows x cols), cols % 32 == 0 (BLOCK: cols % 128 == 0).
-template <int FMT, int MODE, bool BF16, bool FUSED_AMAX, bool DERIVE>
-__global__ __launch_bounds__(256) void cast_rows_kernel(CastArgs a) {
+template <int FMT, int MODE, bool BF16, bool FUSED_AMAX, bool DERIVE, int THREADS>
+__global__ __launch_bounds__(THREADS) void cast_rows_kernel(CastArgs a) {
     const UniformScale u = uniform_scale<FMT, MODE, DERIVE>(a);
     const int64_t cpr = a.cols / 32;
     const int64_t total = a.rows * cpr;
     const size_t esz = BF16 ? 2 : 4;
     uint32_t tmax = 0;
-    for (int64_t base = (int64_t)blockIdx.x * 256; base < total; base += (int64_t)gridDim.x * 256) {
+    for (int64_t base = (int64_t)blockIdx.x * THREADS; base < total; base += (int64_t)gridDim.x * THREADS) {
         const int64_t g = base + threadIdx.x;
         const bool valid = g < total;
         const int64_t gg = valid ? g : total - 1;
@@ -179,40 +193,93 @@ __global__ __launch_bounds__(256) void cast_rows_kernel(CastArgs a) {
             tmax = max(tmax, cm);
         }
     }
-    if (FUSED_AMAX) block_reduce_atomic(tmax, a.amax_out);
+    if (FUSED_AMAX) block_reduce_atomic<THREADS>(tmax, a.amax_out);
 }
 
 // ------------------------------------------------------------------ transposing kernel
 // Input tile 128 rows x 64 cols through LDS; output row = input column.  rows % 32 == 0
-// (BLOCK 1x128: rows % 128 == 0), cols % 8 == 0.
+// (BLOCK 1x128: rows % 128 == 0), cols % 8 == 0.  Thread t then owns output chunk (oc, seg):
+// output row c0 + oc, K values r0 + 32 seg .. +31.
+//
+// bf16 input: the tile is kept as raw bf16 pairs.  Word (c, m) holds rows 2m (low half) and 2m + 1
+// (high half) of column c, at 4-byte index c * 64 + (m ^ 4 h(c)), h(c) = (c ^ c / 8) mod 8: an XOR
+// of whole 16-byte groups, so a chunk is still four aligned 16-byte reads.  A load item is a row
+// pair of one 8-column group; its eight packed words go to eight columns, which h spreads over all
+// banks, and the eight lanes of each 16-byte read pass hit eight different bank groups.
+// fp32 input: word r * 69 + c + 4 (c / 32) + 8 (r / 32) for element (r, c); pitch 69 and the two
+// offsets make both the row writes and the column reads conflict free.
+constexpr int kTPitch = 69;
+__device__ __forceinline__ int tile_word(int r, int c) { return r * kTPitch + c + ((c >> 5) << 2) + ((r >> 5) << 3); }
+constexpr int kTileWords = 127 * kTPitch + 63 + 4 + 24 + 1;
+__device__ __forceinline__ int pair_word(int c, int m) { return c * 64 + (m ^ (((c ^ (c >> 3)) & 7) << 2)); }
+
 template <int FMT, int MODE, bool BF16, bool FUSED_AMAX, bool DERIVE>
 __global__ __launch_bounds__(256) void cast_transposed_kernel(CastArgs a) {
-    __shared__ float tile[128][65];
+    __shared__ __attribute__((aligned(16))) uint32_t tile[BF16 ? 64 * 64 : kTileWords];
     const UniformScale u = uniform_scale<FMT, MODE, DERIVE>(a);
-    const int64_t r0 = (int64_t)blockIdx.y * 128, c0 = (int64_t)blockIdx.x * 64;
-    const size_t esz = BF16 ? 2 : 4;
+    // Block order: groups of `tile_group` row bands; inside a group consecutive workgroups walk down
+    // the bands of one 64-column strip before moving to the next strip.
+    const int64_t ntx = (a.cols + 63) / 64, nty = (a.rows + 127) / 128;
+    const int64_t gy = a.tile_group;
+    const int64_t lin = blockIdx.x;
+    const int64_t grp = lin / (gy * ntx), in = lin - grp * gy * ntx;
+    const int64_t gh = min(gy, nty - grp * gy);
+    const int64_t r0 = (grp * gy + in % gh) * 128, c0 = (in / gh) * 64;
     const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int ch = t + 256 * i;
-        const int rr = ch >> 3, cc = (ch & 7) * 8;
-        float v[8];
-        if (r0 + rr < a.rows && c0 + cc < a.cols) {
-            load8<BF16>(static_cast<const char*>(a.x) + ((r0 + rr) * a.ld + c0 + cc) * esz, v);
-        } else {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) v[k] = 0.0f;
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) tile[rr][cc + k] = v[k];
-    }
-    __syncthreads();
-    const int oc = t >> 2, seg = t & 3;
+    const int oc = ((t >> 5) << 3) | (t & 7), seg = (t >> 3) & 3;
     float v[32];
+    if constexpr (BF16) {
+        const uint16_t* x = static_cast<const uint16_t*>(a.x);
 #pragma unroll
-    for (int j = 0; j < 32; ++j) v[j] = tile[seg * 32 + j][oc];
+        for (int j = 0; j < 2; ++j) {
+            const int it = t + 256 * j, b = it & 7, m = it >> 3;
+            const int64_t r = r0 + 2 * m, c = c0 + 8 * b;
+            uint4 lo = make_uint4(0u, 0u, 0u, 0u), hi = lo;
+            if (c < a.cols) {       // rows are in range: rows % 32 == 0 and the tile band starts below rows
+                if (r < a.rows) lo = *reinterpret_cast<const uint4*>(x + r * a.ld + c);
+                if (r + 1 < a.rows) hi = *reinterpret_cast<const uint4*>(x + (r + 1) * a.ld + c);
+            }
+            const uint32_t wl[4] = {lo.x, lo.y, lo.z, lo.w}, wh[4] = {hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                // column 8b+2k: low halves of both rows; column 8b+2k+1: high halves
+                tile[pair_word(8 * b + 2 * k, m)] = __builtin_amdgcn_perm(wh[k], wl[k], 0x05040100u);
+                tile[pair_word(8 * b + 2 * k + 1, m)] = __builtin_amdgcn_perm(wh[k], wl[k], 0x07060302u);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 w = *reinterpret_cast<const uint4*>(&tile[pair_word(oc, seg * 16 + 4 * i)]);
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                v[8 * i + 2 * d] = bf16lo(ww[d]);
+                v[8 * i + 2 * d + 1] = bf16hi(ww[d]);
+            }
+        }
+    } else {
+        float* tf = reinterpret_cast<float*>(tile);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ch = t + 256 * i;
+            const int rr = ch >> 3, cc = (ch & 7) * 8;
+            float w[8];
+            if (r0 + rr < a.rows && c0 + cc < a.cols) {
+                load8<false>(static_cast<const float*>(a.x) + (r0 + rr) * a.ld + c0 + cc, w);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) w[k] = 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) tf[tile_word(rr, cc + k)] = w[k];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 32; ++j) v[j] = tf[tile_word(seg * 32 + j, oc)];
+    }
     uint32_t out[8], sc = 0, cm = 0;
-    process_chunk<FMT, MODE>(v, u, out, sc, cm);
+    process_chunk<FMT, MODE, 8>(v, u, out, sc, cm);
     const int64_t orow = c0 + oc, k0 = r0 + seg * 32;
     if (orow < a.cols && k0 < a.rows) {
         store32(a.q + orow * a.ldq + k0, out);
@@ -222,7 +289,7 @@ __global__ __launch_bounds__(256) void cast_transposed_kernel(CastArgs a) {
             reinterpret_cast<uint8_t*>(a.scales)[orow * (a.rows / 32) + k0 / 32] = (uint8_t)sc;
         }
     }
-    if (FUSED_AMAX) block_reduce_atomic(cm, a.amax_out);
+    if (FUSED_AMAX) block_reduce_atomic<256>(cm, a.amax_out);
 }
 
 // ------------------------------------------------------------------ 128x128 weight blocks
@@ -334,19 +401,29 @@ static void dispatch_shape(const CastArgs& a, hipStream_t st) {
         }
         const int64_t kmod = MODE == kModeBlock ? 128 : 32;
         if (row_group_ok && a.cols % kmod == 0) {
-            int64_t total = a.rows * (a.cols / 32);
-            int64_t blocks = (total + 255) / 256;
-            int64_t cap = FUSED ? kMaxReduceBlocks : 8192;
-            if (blocks > cap) blocks = cap;
-            hipLaunchKernelGGL((cast_rows_kernel<FMT, MODE, BF16, FUSED, DERIVE>), dim3((unsigned)blocks), dim3(256), 0,
-                               st, a);
+            const int64_t total = a.rows * (a.cols / 32);
+            if (FUSED) {
+                // few large workgroups: each ends with one atomic on the same address
+                int64_t blocks = (total + 1023) / 1024;
+                if (blocks > kMaxReduceBlocks) blocks = kMaxReduceBlocks;
+                hipLaunchKernelGGL((cast_rows_kernel<FMT, MODE, BF16, FUSED, DERIVE, 1024>), dim3((unsigned)blocks),
+                                   dim3(1024), 0, st, a);
+            } else {
+                int64_t blocks = (total + 255) / 256;
+                if (blocks > 8192) blocks = 8192;
+                hipLaunchKernelGGL((cast_rows_kernel<FMT, MODE, BF16, FUSED, DERIVE, 256>), dim3((unsigned)blocks),
+                                   dim3(256), 0, st, a);
+            }
             return;
         }
     } else {
         const int64_t kmod = MODE == kModeBlock ? 128 : 32;
         if (row_group_ok && a.rows % kmod == 0 && a.cols % 8 == 0) {
-            dim3 grid((unsigned)((a.cols + 63) / 64), (unsigned)((a.rows + 127) / 128));
-            hipLaunchKernelGGL((cast_transposed_kernel<FMT, MODE, BF16, FUSED, DERIVE>), grid, dim3(256), 0, st, a);
+            CastArgs b = a;
+            if (b.tile_group <= 0) b.tile_group = 8;
+            const int64_t tiles = ((a.cols + 63) / 64) * ((a.rows + 127) / 128);
+            hipLaunchKernelGGL((cast_transposed_kernel<FMT, MODE, BF16, FUSED, DERIVE>), dim3((unsigned)tiles), dim3(256), 0,
+                               st, b);
             return;
         }
     }
