@@ -91,6 +91,28 @@ __device__ __forceinline__ bool dividends_ok(uint32_t max_abs, uint32_t min_abs_
 // RN(1/s), correctly rounded (IEEE division).
 __device__ __forceinline__ float recip_rn(float s) { return 1.0f / s; }
 
+// Two-term reciprocal for bf16 dividends.  yh is 1/s rounded toward zero, so the residual
+// 1 - s*yh (one fma) is >= 0 and yl = RN(residual * yh) is never negative: then x*yl carries the
+// sign of x and a -0 dividend stays -0 through the fma.  yh + yl lies within about 2^-47 of 1/s,
+// so fma(x, yh, x*yl) is RN(x/s) unless x/s lies that close to a rounding midpoint.  A bf16 x is m * 2^k with m one of 128
+// significands in [1, 2), and every step scales exactly by 2^k while the results stay normal, so
+// checking the 128 significands once decides the question for every bf16 dividend whose quotient
+// (and x*yl) is a normal number; quotients below that are far under the FP8 range anyway.
+__device__ __forceinline__ float recip_hi_rz(float s) {
+    const float y = 1.0f / s;
+    return __builtin_fmaf(-s, y, 1.0f) < 0.0f ? __uint_as_float(__float_as_uint(y) - 1u) : y;
+}
+__device__ __forceinline__ float recip_lo(float s, float yh) { return __builtin_fmaf(-s, yh, 1.0f) * yh; }
+__device__ __forceinline__ float mul2(float x, float yh, float yl) { return __builtin_fmaf(x, yh, x * yl); }
+// Wave-uniform: true when mul2 equals IEEE division by s for all 128 bf16 significands (all lanes of
+// the wave must be active).
+__device__ __forceinline__ bool mul2_exact_bf16(float s, float yh, float yl) {
+    const int lane = threadIdx.x & 63;
+    const float m1 = 1.0f + (float)lane * (1.0f / 128.0f), m2 = m1 + 0.5f;
+    const bool ok = mul2(m1, yh, yl) == m1 / s && mul2(m2, yh, yl) == m2 / s;
+    return __all(ok);
+}
+
 // scale = fl(amax / MAX); 1.0 (or `fallback`) on amax zero / non-finite / underflow.
 template <int FMT>
 __device__ __forceinline__ float scale_from_amax(float amax, float fallback) {

@@ -68,6 +68,19 @@ __device__ __forceinline__ void cast32_div(const float* v, float s, float y, int
     }
 }
 
+// bf16 fast path: element = clip(RN(x / s)) computed as mul2 (valid when mul2_exact_bf16 held for
+// s and the chunk is finite; see common.cuh).
+template <int FMT>
+__device__ __forceinline__ void cast32_mul2(const float* v, float yh, float yl, uint32_t* out) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float c[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) c[k] = clip<FMT>(mul2(v[4 * i + k], yh, yl));
+        out[i] = cvt4<FMT>(c[0], c[1], c[2], c[3]);
+    }
+}
+
 // MX element: clip(x * 2^shift), exact scaling; only NaN needs the slow path.
 template <int FMT>
 __device__ __forceinline__ void cast32_mx(const float* v, int shift, bool has_nan, uint32_t* out) {
@@ -90,20 +103,27 @@ __device__ __forceinline__ void cast32_mx(const float* v, int shift, bool has_na
     }
 }
 
-// Tensor-uniform divisor state (TENSOR and MOSS).
+// Tensor-uniform divisor state (TENSOR and MOSS).  y = RN(1/s) for the one-correction division
+// (ok: s is in its range); two: bf16 inputs may use the two-term reciprocal (yh, yl).
 struct UniformScale {
-    float s, y;
-    bool ok;
+    float s, y, yh, yl;
+    bool ok, two;
 };
 
-template <int FMT, int MODE, bool DERIVE>
+// Called by every thread of the workgroup at kernel start (the bf16 check is a wave vote).
+template <int FMT, int MODE, bool DERIVE, bool BF16>
 __device__ __forceinline__ UniformScale uniform_scale(const CastArgs& a) {
-    UniformScale u{1.0f, 1.0f, true};
+    UniformScale u{1.0f, 1.0f, 1.0f, 0.0f, true, false};
     if (MODE == kModeTensor || MODE == kModeMoss) {
         float s = DERIVE ? scale_from_amax<FMT>(*a.amax_in, 1.0f) : *a.scale_in;
         u.s = s;
         u.y = recip_rn(s);
         u.ok = divisor_ok(s);
+        if (BF16 && u.ok) {
+            u.yh = recip_hi_rz(s);
+            u.yl = recip_lo(s, u.yh);
+            u.two = mul2_exact_bf16(s, u.yh, u.yl);
+        }
         if (DERIVE && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.scale_out = s;
     }
     return u;
@@ -112,13 +132,14 @@ __device__ __forceinline__ UniformScale uniform_scale(const CastArgs& a) {
 // Process one lane chunk v[32] (all 64 lanes of the wave call this together: BLOCK uses shuffles).
 // Returns the per-lane scale value to store (BLOCK: fp32 bits; MX/MOSS: E8M0 byte) in `sc`.
 // BLOCK 1x128: the four chunks of a group sit in lanes l, l ^ G, l ^ 2G, l ^ 3G.
-template <int FMT, int MODE, int G = 1>
+template <int FMT, int MODE, bool BF16, int G = 1>
 __device__ __forceinline__ void process_chunk(const float* v, const UniformScale& u, uint32_t* out,
                                               uint32_t& sc, uint32_t& chunk_max) {
     ChunkStats st = chunk_stats(v);
     chunk_max = st.mx;
     if (MODE == kModeTensor) {
-        cast32_div<FMT, false>(v, u.s, u.y, 0, u.ok && dividends_ok(st.mx, st.mn), out);
+        if (BF16 && u.two && st.mx < 0x7F800000u) cast32_mul2<FMT>(v, u.yh, u.yl, out);
+        else cast32_div<FMT, false>(v, u.s, u.y, 0, u.ok && dividends_ok(st.mx, st.mn), out);
     } else if (MODE == kModeBlock) {
         uint32_t gmx = st.mx;
         uint32_t o = (uint32_t)__shfl_xor((int)gmx, G, 64);
@@ -136,7 +157,13 @@ __device__ __forceinline__ void process_chunk(const float* v, const UniformScale
     } else {  // MOSS
         float s_i = __uint_as_float(st.mx) / fmt_max<FMT>();
         int e = moss_exponent(u.s, s_i);
-        cast32_div<FMT, true>(v, u.s, u.y, -e, u.ok && dividends_ok(st.mx, st.mn) && e > -100, out);
+        // fl(x / S) * 2^-e equals fl(x / (S 2^e)) whenever fl(x / S) is normal; with e > -100 a
+        // subnormal fl(x / S) is below 2^-26 after scaling, i.e. FP8 zero either way
+        const float sg = __builtin_amdgcn_ldexpf(u.s, e);
+        if (BF16 && u.two && e > -100 && divisor_ok(sg) && st.mx < 0x7F800000u)
+            cast32_mul2<FMT>(v, __builtin_amdgcn_ldexpf(u.yh, -e), __builtin_amdgcn_ldexpf(u.yl, -e), out);
+        else
+            cast32_div<FMT, true>(v, u.s, u.y, -e, u.ok && dividends_ok(st.mx, st.mn) && e > -100, out);
         sc = (uint32_t)(e + 127);
     }
 }
@@ -167,7 +194,7 @@ __device__ __forceinline__ void block_reduce_atomic(uint32_t m, float* out) {
 // Output = input layout (rows x cols), cols % 32 == 0 (BLOCK: cols % 128 == 0).
 template <int FMT, int MODE, bool BF16, bool FUSED_AMAX, bool DERIVE, int THREADS>
 __global__ __launch_bounds__(THREADS) void cast_rows_kernel(CastArgs a) {
-    const UniformScale u = uniform_scale<FMT, MODE, DERIVE>(a);
+    const UniformScale u = uniform_scale<FMT, MODE, DERIVE, BF16>(a);
     const int64_t cpr = a.cols / 32;
     const int64_t total = a.rows * cpr;
     const size_t esz = BF16 ? 2 : 4;
@@ -182,7 +209,7 @@ __global__ __launch_bounds__(THREADS) void cast_rows_kernel(CastArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) load8<BF16>(src + j * 8 * esz, v + 8 * j);
         uint32_t out[8], sc = 0, cm = 0;
-        process_chunk<FMT, MODE>(v, u, out, sc, cm);
+        process_chunk<FMT, MODE, BF16>(v, u, out, sc, cm);
         if (valid) {
             store32(a.q + r * a.ldq + c * 32, out);
             if (MODE == kModeBlock) {
@@ -216,7 +243,7 @@ __device__ __forceinline__ int pair_word(int c, int m) { return c * 64 + (m ^ ((
 template <int FMT, int MODE, bool BF16, bool FUSED_AMAX, bool DERIVE>
 __global__ __launch_bounds__(256) void cast_transposed_kernel(CastArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t tile[BF16 ? 64 * 64 : kTileWords];
-    const UniformScale u = uniform_scale<FMT, MODE, DERIVE>(a);
+    const UniformScale u = uniform_scale<FMT, MODE, DERIVE, BF16>(a);
     // Block order: groups of `tile_group` row bands; inside a group consecutive workgroups walk down
     // the bands of one 64-column strip before moving to the next strip.
     const int64_t ntx = (a.cols + 63) / 64, nty = (a.rows + 127) / 128;
@@ -279,7 +306,7 @@ __global__ __launch_bounds__(256) void cast_transposed_kernel(CastArgs a) {
         for (int j = 0; j < 32; ++j) v[j] = tf[tile_word(seg * 32 + j, oc)];
     }
     uint32_t out[8], sc = 0, cm = 0;
-    process_chunk<FMT, MODE, 8>(v, u, out, sc, cm);
+    process_chunk<FMT, MODE, BF16, 8>(v, u, out, sc, cm);
     const int64_t orow = c0 + oc, k0 = r0 + seg * 32;
     if (orow < a.cols && k0 < a.rows) {
         store32(a.q + orow * a.ldq + k0, out);

@@ -244,13 +244,18 @@ def test_all_bf16_patterns_and_midpoint_quotients(fq, orc, fmt):
     fast path must agree with IEEE division there)."""
     allb = np.arange(65536, dtype=np.uint16).reshape(256, 256)
     xd = to_dev(allb)
-    for s in (1.0, 0.0123, 3.7e-5, 7.1e9, 2.0 ** -70):
+    # 0x3AFFFFFF and 0x3D61368B: scales whose two-term reciprocal is off for some bf16 significand
+    # (1/s sits next to a rounding midpoint), so the bf16 casts must take the exact division there;
+    # 0x3DB6DB6E: RN(1/s) > 1/s, where a careless two-term product turns -0 into +0
+    odd = [float(np.array([b], np.uint32).view(np.float32)[0]) for b in (0x3AFFFFFF, 0x3D61368B, 0x3DB6DB6E)]
+    for s in [1.0, 0.0123, 3.7e-5, 7.1e9, 2.0 ** -70] + odd:
         sd = torch.tensor([s], dtype=torch.float32, device=DEV)
-        q, _, _, _ = fq.quantize(xd, TENSOR, fmt, tensor_scale=sd, scale_is_input=True)
-        assert same(host(q), orc.quantize_tensor(allb, fmt, s)), s
-        q, e, _, _ = fq.quantize(xd, MOSS, fmt, tensor_scale=sd, scale_is_input=True)
-        oq, oe = orc.quantize_moss_given(allb, fmt, s)
-        assert same(host(e), oe) and same(host(q), oq), s
+        for tr in (False, True):
+            q, _, _, _ = fq.quantize(xd, TENSOR, fmt, tensor_scale=sd, scale_is_input=True, transpose_out=tr)
+            assert same(host(q), orc.quantize_tensor(allb, fmt, s, transpose=tr)), (s, tr)
+            q, e, _, _ = fq.quantize(xd, MOSS, fmt, tensor_scale=sd, scale_is_input=True, transpose_out=tr)
+            oq, oe = orc.quantize_moss_given(allb, fmt, s, transpose=tr)
+            assert same(host(e), oe) and same(host(q), oq), (s, tr)
     q, e, _, _ = fq.quantize(xd, MX, fmt)
     oq, oe = orc.quantize_mx(allb, fmt)
     assert same(host(e), oe) and same(host(q), oq)
@@ -267,6 +272,11 @@ def test_all_bf16_patterns_and_midpoint_quotients(fq, orc, fmt):
         sd = torch.tensor([s], dtype=torch.float32, device=DEV)
         q, _, _, _ = fq.quantize(to_dev(xs), TENSOR, fmt, tensor_scale=sd, scale_is_input=True)
         assert same(host(q), orc.quantize_tensor(xs, fmt, s)), s
+        # bf16 dividends next to the same midpoints (the two-term reciprocal path)
+        xb = workloads.to_bf16_bits(xs)
+        xb = np.concatenate([xb, (xb.astype(np.int64) + 1).astype(np.uint16), (xb.astype(np.int64) - 1).astype(np.uint16)])
+        q, _, _, _ = fq.quantize(to_dev(xb), TENSOR, fmt, tensor_scale=sd, scale_is_input=True)
+        assert same(host(q), orc.quantize_tensor(xb, fmt, s)), s
 
 
 def test_cast_determinism(fq):
