@@ -6,8 +6,9 @@ One step runs every scaling scheme's full path on its workload, with all inputs 
                        GEMM (bf16 out), then both amax-history updates
   fine-grained         X 4096x7168 (1x128) and W 2048x7168 (128x128) casts, block-scaled GEMM
   MXFP8                A, B 8192x8192 casts, E8M0-scaled GEMM
-  MOSS fwd+bwd         X 16384x4096, W 4096x4096 (E4M3), dY 16384x4096 (E5M2): six casts
-                       (each tensor along both axes), Y = X W^T, dX = dY W, dW = dY^T X
+  MOSS fwd+bwd         X 16384x4096, W 4096x4096 (E4M3), dY 16384x4096 (E5M2): amax, then one
+                       dual-axis cast per tensor (both quantized copies in one pass),
+                       Y = X W^T, dX = dY W, dW = dY^T X
 The headline value is the step's total GEMM flops (2 M N K per GEMM) divided by the step time,
 i.e. scaled-GEMM TFLOP/s including every quantization the path performs.
 
@@ -165,7 +166,7 @@ def main():
     o["Y5"], o["dX5"], o["dW5"] = zeros((16384, 4096), bf16), zeros((16384, 4096), bf16), zeros((4096, 4096), bf16)
 
     timer = Timer(torch)
-    Q, G_ = fq.fp8_quantize, fq.fp8_scaled_gemm
+    Q, QD, G_ = fq.fp8_quantize, fq.fp8_quantize_dual, fq.fp8_scaled_gemm
 
     def step(i):
         # per-tensor current scaling
@@ -188,9 +189,8 @@ def main():
         timer("g4", lambda: G_(MX, o["q4a"], E4M3, o["e4a"], o["q4b"], E4M3, o["e4b"], None, None, o["C4"], fq.OUT_BF16))
         # MOSS forward + backward
         for n, fmt in (("X", E4M3), ("W", E4M3), ("G", E5M2)):
-            timer("q5", lambda: Q(MOSS, fmt, w5[n], o["q5" + n], o["e5" + n], o["S5" + n], False, o["m5" + n]))
-            timer("q5T", lambda: Q(MOSS, fmt, w5[n], o["q5" + n + "T"], o["e5" + n + "T"], o["S5" + n], True,
-                                   transpose_out=True))
+            timer("q5", lambda: QD(MOSS, fmt, w5[n], o["q5" + n], o["e5" + n], o["q5" + n + "T"], o["e5" + n + "T"],
+                                   o["S5" + n], False, o["m5" + n]))
         timer("g5", lambda: G_(MOSS, o["q5X"], E4M3, o["e5X"], o["q5W"], E4M3, o["e5W"], o["S5X"], o["S5W"], o["Y5"], fq.OUT_BF16))
         timer("g5", lambda: G_(MOSS, o["q5G"], E5M2, o["e5G"], o["q5WT"], E4M3, o["e5WT"], o["S5G"], o["S5W"], o["dX5"], fq.OUT_BF16))
         timer("g5", lambda: G_(MOSS, o["q5GT"], E5M2, o["e5GT"], o["q5XT"], E4M3, o["e5XT"], o["S5G"], o["S5X"], o["dW5"], fq.OUT_BF16))
@@ -208,10 +208,9 @@ def main():
         "q3x": 4096 * 7168 * 3 + 4096 * 56 * 4,
         "q3w": 2048 * 7168 * 3 + 16 * 56 * 4,
         "q4": 2 * (8192 * 8192 * 3 + 8192 * 256),
-        "q5": MOSS_ELEMS * (2 + 2 + 1) + MOSS_ELEMS // 32,
-        "q5T": MOSS_ELEMS * (2 + 1) + MOSS_ELEMS // 32,
+        "q5": MOSS_ELEMS * (2 + 2 + 1 + 1) + 2 * (MOSS_ELEMS // 32),     # amax read + one read, two copies
     }
-    qcalls = {"q1": 1, "q2": 1, "q3x": 1, "q3w": 1, "q4": 1, "q5": 3, "q5T": 3}
+    qcalls = {"q1": 1, "q2": 1, "q3x": 1, "q3w": 1, "q4": 1, "q5": 3}
 
     # ---------------- warmup, then the timed steps
     for i in range(args.warmup):

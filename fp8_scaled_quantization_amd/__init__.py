@@ -5,8 +5,8 @@ binding is imported on first use of any library name, and raises ImportError if 
 not been built: there is no fallback path.  `workloads` (seeded synthetic inputs) imports without it.
 """
 _LIB_NAMES = ("BLOCK", "E4M3", "E5M2", "IN_BF16", "IN_F32", "MOSS", "MX", "OUT_BF16", "OUT_F32", "TENSOR",
-              "Fp8qError", "fp8_amax", "fp8_history_update", "fp8_quantize", "fp8_scaled_gemm", "init",
-              "quantize", "scaled_gemm")
+              "Fp8qError", "fp8_amax", "fp8_history_update", "fp8_quantize", "fp8_quantize_dual", "fp8_scaled_gemm",
+              "init", "quantize", "quantize_dual", "scaled_gemm")
 
 __all__ = list(_LIB_NAMES)
 

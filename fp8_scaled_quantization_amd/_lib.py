@@ -20,7 +20,8 @@ IN_F32, IN_BF16 = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
 TENSOR, BLOCK, MX, MOSS = 0, 1, 2, 3
 
-EXPORTS = ("fp8q_init", "fp8q_last_error", "fp8_amax", "fp8_quantize", "fp8_history_update", "fp8_scaled_gemm")
+EXPORTS = ("fp8q_init", "fp8q_last_error", "fp8_amax", "fp8_quantize", "fp8_quantize_dual", "fp8_history_update",
+           "fp8_scaled_gemm")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libfp8q.so is not built (run __graft_entry__.build() or "
@@ -36,6 +37,8 @@ _L.fp8_amax.restype = _I
 _L.fp8_amax.argtypes = [_P, _I, _I64, _I64, _I64, _P, _P]
 _L.fp8_quantize.restype = _I
 _L.fp8_quantize.argtypes = [_I, _I, _P, _I, _I64, _I64, _I64, _I, _I, _I, _P, _I64, _P, _P, _I, _P, _P]
+_L.fp8_quantize_dual.restype = _I
+_L.fp8_quantize_dual.argtypes = [_I, _I, _P, _I, _I64, _I64, _I64, _P, _I64, _P, _P, _I64, _P, _P, _I, _P, _P]
 _L.fp8_history_update.restype = _I
 _L.fp8_history_update.argtypes = [_P, _I64, _P, _P, _I, _P]
 _L.fp8_scaled_gemm.restype = _I
@@ -85,7 +88,7 @@ def init() -> None:
     _check(_L.fp8q_init())
 
 
-# ------------------------------------------------------------------ the four entry points
+# ------------------------------------------------------------------ the entry points
 def fp8_amax(x: torch.Tensor, amax_out: torch.Tensor, stream=None) -> None:
     _check(_L.fp8_amax(_ptr(x), _in_kind(x), x.shape[0], x.shape[1], _ld(x), _ptr(amax_out), _stream(stream)))
 
@@ -99,6 +102,15 @@ def fp8_quantize(mode: int, fmt: int, x: torch.Tensor, q: torch.Tensor, scales=N
                            int(block[0]), int(block[1]), int(bool(transpose_out)), _ptr(q), _ld(q),
                            _ptr(scales), _ptr(tensor_scale), int(bool(scale_is_input)), _ptr(amax_out),
                            _stream(stream)))
+
+
+def fp8_quantize_dual(mode: int, fmt: int, x: torch.Tensor, q: torch.Tensor, scales, qt: torch.Tensor, scales_t,
+                      tensor_scale=None, scale_is_input: bool = False, amax_out=None, stream=None) -> None:
+    if q.dtype != torch.uint8 or qt.dtype != torch.uint8:
+        raise TypeError("q and qt must be uint8")
+    _check(_L.fp8_quantize_dual(mode, fmt, _ptr(x), _in_kind(x), x.shape[0], x.shape[1], _ld(x),
+                                _ptr(q), _ld(q), _ptr(scales), _ptr(qt), _ld(qt), _ptr(scales_t),
+                                _ptr(tensor_scale), int(bool(scale_is_input)), _ptr(amax_out), _stream(stream)))
 
 
 def fp8_history_update(history: torch.Tensor, amax_new: torch.Tensor, scale: torch.Tensor, fmt: int,
@@ -138,6 +150,24 @@ def quantize(x: torch.Tensor, mode: int, fmt: int, block=(1, 128), transpose_out
         amax_out = torch.zeros(1, dtype=torch.float32, device=x.device)
     fp8_quantize(mode, fmt, x, q, scales, tensor_scale, scale_is_input, amax_out, block, transpose_out, stream)
     return q, scales, tensor_scale, amax_out
+
+
+def quantize_dual(x: torch.Tensor, mode: int, fmt: int, tensor_scale=None, scale_is_input: bool = False,
+                  amax_out=None, stream=None):
+    """Allocate both copies and call fp8_quantize_dual.  Returns (q, scales, qt, scales_t, tensor_scale, amax)."""
+    R, C = x.shape
+    q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    qt = torch.empty((C, R), dtype=torch.uint8, device=x.device)
+    shp, dt = scale_shape(mode, R, C)
+    shpt, _ = scale_shape(mode, C, R)
+    scales = torch.empty(shp, dtype=dt, device=x.device) if shp is not None else None
+    scales_t = torch.empty(shpt, dtype=dt, device=x.device) if shpt is not None else None
+    if mode in (TENSOR, MOSS) and tensor_scale is None:
+        tensor_scale = torch.ones(1, dtype=torch.float32, device=x.device)
+    if mode in (TENSOR, MOSS) and not scale_is_input and amax_out is None:
+        amax_out = torch.zeros(1, dtype=torch.float32, device=x.device)
+    fp8_quantize_dual(mode, fmt, x, q, scales, qt, scales_t, tensor_scale, scale_is_input, amax_out, stream)
+    return q, scales, qt, scales_t, tensor_scale, amax_out
 
 
 def scaled_gemm(mode: int, A, afmt, Ascale, B, bfmt, Bscale, Aglobal=None, Bglobal=None,

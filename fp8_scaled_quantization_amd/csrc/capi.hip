@@ -139,6 +139,83 @@ int fp8_quantize(int mode, int fmt, const void* x, int in_dtype, int64_t rows, i
     return check_launch("fp8_quantize");
 }
 
+int fp8_quantize_dual(int mode, int fmt, const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld,
+                      uint8_t* q, int64_t ldq, void* scales, uint8_t* qt, int64_t ldqt, void* scales_t,
+                      float* tensor_scale, int scale_is_input, float* amax_out, void* stream) {
+    g_err[0] = 0;
+    if (mode != FP8Q_TENSOR && mode != FP8Q_MX && mode != FP8Q_MOSS)
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize_dual: mode %d is not FP8Q_TENSOR/MX/MOSS", mode);
+    if (!valid_fmt(fmt)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize_dual: fmt %d is not FP8Q_E4M3/E5M2", fmt);
+    if (!valid_in(in_dtype)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize_dual: in_dtype %d is not FP8Q_IN_F32/BF16", in_dtype);
+    if (rows < 0 || cols < 0 || ld < cols)
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize_dual: bad shape rows=%lld cols=%lld ld=%lld", (long long)rows,
+                    (long long)cols, (long long)ld);
+    if (ldq < cols || ldqt < rows)
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize_dual: ldq=%lld / ldqt=%lld smaller than cols=%lld / rows=%lld",
+                    (long long)ldq, (long long)ldqt, (long long)cols, (long long)rows);
+    const bool empty = rows * cols == 0;
+    if (!empty && (!x || !q || !qt)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize_dual: NULL x, q or qt");
+    if (mode != FP8Q_TENSOR && !empty && (!scales || !scales_t))
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize_dual: NULL scales or scales_t");
+    const bool needs_amax = (mode == FP8Q_TENSOR || mode == FP8Q_MOSS) && !scale_is_input;
+    if ((mode == FP8Q_TENSOR || mode == FP8Q_MOSS) && !tensor_scale)
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize_dual: tensor_scale is required for TENSOR and MOSS");
+    if (needs_amax && !amax_out)
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize_dual: amax_out is required when the scale is derived");
+    if (cols % 8 || ld % 8 || !aligned16(x))
+        return fail(FP8Q_ERR_UNSUPPORTED, "fp8_quantize_dual: needs cols %% 8 == 0, ld %% 8 == 0 and a 16-byte aligned x");
+    const bool one_pass = rows % 32 == 0 && cols % 32 == 0 && ldq % 16 == 0 && ldqt % 16 == 0 && aligned16(q) &&
+                          aligned16(qt);
+    if (!one_pass) {
+        // the two single-copy casts; the second uses the scale the first one used or derived
+        int rc = fp8_quantize(mode, fmt, x, in_dtype, rows, cols, ld, 1, 1, 0, q, ldq, scales, tensor_scale,
+                              scale_is_input, amax_out, stream);
+        if (rc) return rc;
+        return fp8_quantize(mode, fmt, x, in_dtype, rows, cols, ld, 1, 1, 1, qt, ldqt, scales_t, tensor_scale,
+                            mode == FP8Q_MX ? 0 : 1, nullptr, stream);
+    }
+    int rc = check_device();
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool bf16 = in_dtype == FP8Q_IN_BF16;
+    if (needs_amax && empty) {
+        fp8q::launch_fill_f32(amax_out, 0.0f, st);
+        fp8q::launch_fill_f32(tensor_scale, 1.0f, st);
+        return check_launch("fp8_quantize_dual");
+    }
+    fp8q::CastArgs a{};
+    a.mode = mode;
+    a.fmt = fmt;
+    a.x = x;
+    a.bf16 = bf16;
+    a.rows = rows;
+    a.cols = cols;
+    a.ld = ld;
+    a.transpose = true;
+    a.q = qt;
+    a.ldq = ldqt;
+    a.scales = scales_t;
+    a.q2 = q;
+    a.ldq2 = ldq;
+    a.scales2 = scales;
+    a.vec_out = true;
+    if (mode == FP8Q_TENSOR || mode == FP8Q_MOSS) {
+        if (needs_amax) {
+            fp8q::launch_amax(x, bf16, rows, cols, ld, amax_out, st);
+            a.amax_in = amax_out;
+            a.scale_out = tensor_scale;
+        } else {
+            a.scale_in = tensor_scale;
+            if (mode == FP8Q_TENSOR && amax_out) {
+                fp8q::launch_zero_u32(amax_out, st);
+                a.amax_out = amax_out;
+            }
+        }
+    }
+    fp8q::launch_cast_dual(a, st);
+    return check_launch("fp8_quantize_dual");
+}
+
 int fp8_history_update(float* history, int64_t len, const float* amax_new, float* scale_inout, int fmt, void* stream) {
     g_err[0] = 0;
     if (!valid_fmt(fmt)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_history_update: fmt %d is not FP8Q_E4M3/E5M2", fmt);

@@ -142,6 +142,34 @@ __device__ __forceinline__ int mx_exponent(float amax) {
     return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
+// fl(a / MAX) for a >= 0: the one-correction division where its guards hold, else IEEE division.
+template <int FMT>
+__device__ __forceinline__ float div_by_max(float a) {
+    const uint32_t b = __float_as_uint(a);
+    if (b >= 0x0F800000u && b <= 0x5D800000u) return div_fast(a, fmt_max<FMT>(), 1.0f / fmt_max<FMT>());
+    return a / fmt_max<FMT>();
+}
+
+// S = ms * 2^ES, computed once per tensor for moss_exponent_p.
+struct SParts {
+    int ES;
+    uint32_t ms;
+};
+__device__ __forceinline__ SParts s_parts(float S) {
+    SParts p;
+    p.ES = norm_exp(S, p.ms);
+    return p;
+}
+// moss_exponent(S, s_i) with S given by its parts.
+__device__ __forceinline__ int moss_exponent_p(const SParts& p, float s_i) {
+    if (!(s_i > 0.0f)) return s_i == 0.0f ? -127 : 0;         // NaN -> 0
+    if (__float_as_uint(s_i) >= 0x7F800000u) return 0;
+    uint32_t mi;
+    int Ei = norm_exp(s_i, mi);
+    int e = Ei - p.ES + (mi > p.ms ? 1 : 0);
+    return e < -127 ? -127 : (e > 0 ? 0 : e);
+}
+
 // MOSS: smallest e in [-127, 0] with S * 2^e >= s_i (0 if none), S > 0 finite.
 __device__ __forceinline__ int moss_exponent(float S, float s_i) {
     if (!(s_i > 0.0f)) return s_i == 0.0f ? -127 : 0;         // NaN -> 0

@@ -31,7 +31,14 @@ struct CastArgs {
     float* scale_out;                // written by workgroup 0 when the scale is derived here
     float* amax_out;                 // fused amax (TENSOR with a given scale), may be null
     int tile_group;                  // transposed kernel: 128-row tile bands walked per column strip
+    uint8_t* q2;                     // dual cast: the non-transposed copy (rows x cols), row stride ldq2,
+    int64_t ldq2;                    //   with its E8M0 scales (MX, MOSS) in scales2 [rows][cols / 32];
+    void* scales2;                   //   q / ldq / scales then hold the transposed copy
 };
+
+// Both copies of x in one pass (TENSOR, MX, MOSS; rows % 32 == 0, cols % 32 == 0, vector-aligned
+// outputs): q2 gets the row-grouped copy, q the transposed one.
+int launch_cast_dual(const CastArgs& a, hipStream_t st);
 
 // Casts with the tensor scale (or S) either given (scale_in) or derived from amax_in.
 int launch_cast(const CastArgs& a, hipStream_t st);

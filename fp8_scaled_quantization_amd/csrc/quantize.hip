@@ -22,28 +22,32 @@
 namespace fp8q {
 
 // ------------------------------------------------------------------ per-chunk work
-struct ChunkStats {
-    uint32_t mx;      // max |x| bits
-    uint32_t mn;      // min (|x| bits - 1), zero wraps to 0xffffffff
-};
-
-__device__ __forceinline__ ChunkStats chunk_stats(const float* v) {
-    ChunkStats s{0u, 0xFFFFFFFFu};
+// Elements are cast N at a time (N = 32: one lane chunk; N = 8: one 16-byte bf16 load); out[i]
+// packs the codes of v[4i .. 4i+3].
+// max |x| bits of N values
+template <int N>
+__device__ __forceinline__ uint32_t chunk_max(const float* v) {
+    uint32_t m = 0u;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-        uint32_t b = absbits(v[j]);
-        s.mx = max(s.mx, b);
-        s.mn = min(s.mn, b - 1u);
-    }
-    return s;
+    for (int j = 0; j < N; ++j) m = max(m, absbits(v[j]));
+    return m;
+}
+// min (|x| bits - 1) of N values (zero wraps to 0xffffffff): the small-dividend guard of the
+// one-correction division; only its paths compute it
+template <int N>
+__device__ __forceinline__ uint32_t chunk_min_m1(const float* v) {
+    uint32_t m = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < N; ++j) m = min(m, absbits(v[j]) - 1u);
+    return m;
 }
 
-// out[i] packs codes of v[4i .. 4i+3]: element = clip(fl(v/s) * 2^shift).
-template <int FMT, bool SHIFT>
-__device__ __forceinline__ void cast32_div(const float* v, float s, float y, int shift, bool fast, uint32_t* out) {
+// element = clip(fl(v/s) * 2^shift); `fast` selects the one-correction division (its guards hold).
+template <int FMT, bool SHIFT, int N>
+__device__ __forceinline__ void cast_div(const float* v, float s, float y, int shift, bool fast, uint32_t* out) {
     if (fast) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < N / 4; ++i) {
             float c[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -55,7 +59,7 @@ __device__ __forceinline__ void cast32_div(const float* v, float s, float y, int
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < N / 4; ++i) {
             uint32_t w = 0;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -69,11 +73,11 @@ __device__ __forceinline__ void cast32_div(const float* v, float s, float y, int
 }
 
 // bf16 fast path: element = clip(RN(x / s)) computed as mul2 (valid when mul2_exact_bf16 held for
-// s and the chunk is finite; see common.cuh).
-template <int FMT>
-__device__ __forceinline__ void cast32_mul2(const float* v, float yh, float yl, uint32_t* out) {
+// s and the values are finite; see common.cuh).
+template <int FMT, int N>
+__device__ __forceinline__ void cast_mul2(const float* v, float yh, float yl, uint32_t* out) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < N / 4; ++i) {
         float c[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) c[k] = clip<FMT>(mul2(v[4 * i + k], yh, yl));
@@ -82,11 +86,11 @@ __device__ __forceinline__ void cast32_mul2(const float* v, float yh, float yl, 
 }
 
 // MX element: clip(x * 2^shift), exact scaling; only NaN needs the slow path.
-template <int FMT>
-__device__ __forceinline__ void cast32_mx(const float* v, int shift, bool has_nan, uint32_t* out) {
+template <int FMT, int N>
+__device__ __forceinline__ void cast_mx(const float* v, int shift, bool has_nan, uint32_t* out) {
     if (!has_nan) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < N / 4; ++i) {
             float c[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) c[k] = clip<FMT>(__builtin_amdgcn_ldexpf(v[4 * i + k], shift));
@@ -94,7 +98,7 @@ __device__ __forceinline__ void cast32_mx(const float* v, int shift, bool has_na
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < N / 4; ++i) {
             uint32_t w = 0;
 #pragma unroll
             for (int k = 0; k < 4; ++k) w |= code_slow<FMT>(__builtin_amdgcn_ldexpf(v[4 * i + k], shift)) << (8 * k);
@@ -108,12 +112,13 @@ __device__ __forceinline__ void cast32_mx(const float* v, int shift, bool has_na
 struct UniformScale {
     float s, y, yh, yl;
     bool ok, two;
+    SParts sp;        // MOSS: S as mantissa and exponent
 };
 
 // Called by every thread of the workgroup at kernel start (the bf16 check is a wave vote).
 template <int FMT, int MODE, bool DERIVE, bool BF16>
 __device__ __forceinline__ UniformScale uniform_scale(const CastArgs& a) {
-    UniformScale u{1.0f, 1.0f, 1.0f, 0.0f, true, false};
+    UniformScale u{1.0f, 1.0f, 1.0f, 0.0f, true, false, {0, 0u}};
     if (MODE == kModeTensor || MODE == kModeMoss) {
         float s = DERIVE ? scale_from_amax<FMT>(*a.amax_in, 1.0f) : *a.scale_in;
         u.s = s;
@@ -124,9 +129,36 @@ __device__ __forceinline__ UniformScale uniform_scale(const CastArgs& a) {
             u.yl = recip_lo(s, u.yh);
             u.two = mul2_exact_bf16(s, u.yh, u.yl);
         }
+        if (MODE == kModeMoss) u.sp = s_parts(s);
         if (DERIVE && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.scale_out = s;
     }
     return u;
+}
+
+// TENSOR / MX / MOSS cast of N values of one 32-group: gmx is the group's max |x| bits, lmx the
+// max of these N values (the division path is chosen per lane; the result does not depend on it).
+// Returns the E8M0 byte (MX, MOSS) in sc.
+template <int FMT, int MODE, bool BF16, int N>
+__device__ __forceinline__ void cast_group(const float* v, uint32_t gmx, uint32_t lmx, const UniformScale& u,
+                                           uint32_t* out, uint32_t& sc) {
+    if (MODE == kModeTensor) {
+        if (BF16 && u.two && lmx < 0x7F800000u) cast_mul2<FMT, N>(v, u.yh, u.yl, out);
+        else cast_div<FMT, false, N>(v, u.s, u.y, 0, u.ok && dividends_ok(lmx, chunk_min_m1<N>(v)), out);
+    } else if (MODE == kModeMX) {
+        int e = mx_exponent<FMT>(__uint_as_float(gmx));
+        cast_mx<FMT, N>(v, -e, lmx > 0x7F800000u, out);
+        sc = (uint32_t)(e + 127);
+    } else {  // MOSS
+        const int e = moss_exponent_p(u.sp, div_by_max<FMT>(__uint_as_float(gmx)));
+        // fl(x / S) * 2^-e equals fl(x / (S 2^e)) whenever fl(x / S) is normal; with e > -100 a
+        // subnormal fl(x / S) is below 2^-26 after scaling, i.e. FP8 zero either way
+        const float sg = __builtin_amdgcn_ldexpf(u.s, e);
+        if (BF16 && u.two && e > -100 && divisor_ok(sg) && lmx < 0x7F800000u)
+            cast_mul2<FMT, N>(v, __builtin_amdgcn_ldexpf(u.yh, -e), __builtin_amdgcn_ldexpf(u.yl, -e), out);
+        else
+            cast_div<FMT, true, N>(v, u.s, u.y, -e, u.ok && dividends_ok(lmx, chunk_min_m1<N>(v)) && e > -100, out);
+        sc = (uint32_t)(e + 127);
+    }
 }
 
 // Process one lane chunk v[32] (all 64 lanes of the wave call this together: BLOCK uses shuffles).
@@ -134,37 +166,21 @@ __device__ __forceinline__ UniformScale uniform_scale(const CastArgs& a) {
 // BLOCK 1x128: the four chunks of a group sit in lanes l, l ^ G, l ^ 2G, l ^ 3G.
 template <int FMT, int MODE, bool BF16, int G = 1>
 __device__ __forceinline__ void process_chunk(const float* v, const UniformScale& u, uint32_t* out,
-                                              uint32_t& sc, uint32_t& chunk_max) {
-    ChunkStats st = chunk_stats(v);
-    chunk_max = st.mx;
-    if (MODE == kModeTensor) {
-        if (BF16 && u.two && st.mx < 0x7F800000u) cast32_mul2<FMT>(v, u.yh, u.yl, out);
-        else cast32_div<FMT, false>(v, u.s, u.y, 0, u.ok && dividends_ok(st.mx, st.mn), out);
-    } else if (MODE == kModeBlock) {
-        uint32_t gmx = st.mx;
+                                              uint32_t& sc, uint32_t& chunk_max_out) {
+    const uint32_t mx = chunk_max<32>(v);
+    chunk_max_out = mx;
+    if (MODE == kModeBlock) {
+        uint32_t gmx = mx;
         uint32_t o = (uint32_t)__shfl_xor((int)gmx, G, 64);
         gmx = max(gmx, o);
         o = (uint32_t)__shfl_xor((int)gmx, 2 * G, 64);
         gmx = max(gmx, o);
         float s = scale_from_amax<FMT>(__uint_as_float(gmx), 1.0f);
         float y = recip_rn(s);
-        cast32_div<FMT, false>(v, s, y, 0, divisor_ok(s) && dividends_ok(st.mx, st.mn), out);
+        cast_div<FMT, false, 32>(v, s, y, 0, divisor_ok(s) && dividends_ok(mx, chunk_min_m1<32>(v)), out);
         sc = __float_as_uint(s);
-    } else if (MODE == kModeMX) {
-        int e = mx_exponent<FMT>(__uint_as_float(st.mx));
-        cast32_mx<FMT>(v, -e, st.mx > 0x7F800000u, out);
-        sc = (uint32_t)(e + 127);
-    } else {  // MOSS
-        float s_i = __uint_as_float(st.mx) / fmt_max<FMT>();
-        int e = moss_exponent(u.s, s_i);
-        // fl(x / S) * 2^-e equals fl(x / (S 2^e)) whenever fl(x / S) is normal; with e > -100 a
-        // subnormal fl(x / S) is below 2^-26 after scaling, i.e. FP8 zero either way
-        const float sg = __builtin_amdgcn_ldexpf(u.s, e);
-        if (BF16 && u.two && e > -100 && divisor_ok(sg) && st.mx < 0x7F800000u)
-            cast32_mul2<FMT>(v, __builtin_amdgcn_ldexpf(u.yh, -e), __builtin_amdgcn_ldexpf(u.yl, -e), out);
-        else
-            cast32_div<FMT, true>(v, u.s, u.y, -e, u.ok && dividends_ok(st.mx, st.mn) && e > -100, out);
-        sc = (uint32_t)(e + 127);
+    } else {
+        cast_group<FMT, MODE, BF16, 32>(v, mx, mx, u, out, sc);
     }
 }
 
@@ -224,34 +240,56 @@ __global__ __launch_bounds__(THREADS) void cast_rows_kernel(CastArgs a) {
 }
 
 // ------------------------------------------------------------------ transposing kernel
-// Input tile 128 rows x 64 cols through LDS; output row = input column.  rows % 32 == 0
-// (BLOCK 1x128: rows % 128 == 0), cols % 8 == 0.  Thread t then owns output chunk (oc, seg):
-// output row c0 + oc, K values r0 + 32 seg .. +31.
+// Tile of 128 input rows x 64 input columns through LDS, 256 threads; output row = input column.
+// rows % 32 == 0 (BLOCK 1x128: rows % 128 == 0), cols % 8 == 0.  Thread t then owns output chunk
+// (oc, seg): output row c0 + oc, K values r0 + 32 seg .. +31, so every output row gets 128
+// contiguous bytes from one workgroup.  (A 128 x 128 tile with 512 threads, which also makes the
+// dual cast's row-grouped stores whole lines, measured slower.)
 //
 // bf16 input: the tile is kept as raw bf16 pairs.  Word (c, m) holds rows 2m (low half) and 2m + 1
 // (high half) of column c, at 4-byte index c * 64 + (m ^ 4 h(c)), h(c) = (c ^ c / 8) mod 8: an XOR
 // of whole 16-byte groups, so a chunk is still four aligned 16-byte reads.  A load item is a row
-// pair of one 8-column group; its eight packed words go to eight columns, which h spreads over all
-// banks, and the eight lanes of each 16-byte read pass hit eight different bank groups.
+// pair of one 8-column group; a half-wave covers 8 column groups x 4 row pairs, whose eight packed
+// words per column land in 32 different banks, and the eight lanes of each 16-byte read pass hit
+// eight different bank groups.
 // fp32 input: word r * 69 + c + 4 (c / 32) + 8 (r / 32) for element (r, c); pitch 69 and the two
 // offsets make both the row writes and the column reads conflict free.
 constexpr int kTPitch = 69;
 __device__ __forceinline__ int tile_word(int r, int c) { return r * kTPitch + c + ((c >> 5) << 2) + ((r >> 5) << 3); }
 constexpr int kTileWords = 127 * kTPitch + 63 + 4 + 24 + 1;
 __device__ __forceinline__ int pair_word(int c, int m) { return c * 64 + (m ^ (((c ^ (c >> 3)) & 7) << 2)); }
+constexpr int kTileCols = 64, kTileThreads = 256;
 
-template <int FMT, int MODE, bool BF16, bool FUSED_AMAX, bool DERIVE>
-__global__ __launch_bounds__(256) void cast_transposed_kernel(CastArgs a) {
-    __shared__ __attribute__((aligned(16))) uint32_t tile[BF16 ? 64 * 64 : kTileWords];
+// Row-grouped cast of 8 values of one row inside the transposed kernel's load phase (dual cast):
+// the 32-group is the four lanes l ^ 0..3; all lanes call this together.
+template <int FMT, int MODE, bool BF16>
+__device__ __forceinline__ void dual_row8(const float* v8, int64_t row, int64_t c, const UniformScale& u, const CastArgs& a) {
+    const uint32_t lmx = chunk_max<8>(v8);
+    uint32_t g = lmx;
+    g = max(g, (uint32_t)__shfl_xor((int)g, 1, 64));
+    g = max(g, (uint32_t)__shfl_xor((int)g, 2, 64));
+    uint32_t o[2], sc = 0;
+    cast_group<FMT, MODE, BF16, 8>(v8, g, lmx, u, o, sc);
+    if (row < a.rows && c < a.cols) {
+        *reinterpret_cast<uint2*>(a.q2 + row * a.ldq2 + c) = make_uint2(o[0], o[1]);
+        if ((MODE == kModeMX || MODE == kModeMoss) && (c & 31) == 0)
+            reinterpret_cast<uint8_t*>(a.scales2)[row * (a.cols / 32) + c / 32] = (uint8_t)sc;
+    }
+}
+
+template <int FMT, int MODE, bool BF16, bool FUSED_AMAX, bool DERIVE, bool DUAL>
+__global__ __launch_bounds__(kTileThreads) void cast_transposed_kernel(CastArgs a) {
+    constexpr int TC = kTileCols, NT = kTileThreads;
+    __shared__ __attribute__((aligned(16))) uint32_t tile[BF16 ? TC * 64 : kTileWords];
     const UniformScale u = uniform_scale<FMT, MODE, DERIVE, BF16>(a);
     // Block order: groups of `tile_group` row bands; inside a group consecutive workgroups walk down
-    // the bands of one 64-column strip before moving to the next strip.
-    const int64_t ntx = (a.cols + 63) / 64, nty = (a.rows + 127) / 128;
+    // the bands of one column strip before moving to the next strip.
+    const int64_t ntx = (a.cols + TC - 1) / TC, nty = (a.rows + 127) / 128;
     const int64_t gy = a.tile_group;
     const int64_t lin = blockIdx.x;
     const int64_t grp = lin / (gy * ntx), in = lin - grp * gy * ntx;
     const int64_t gh = min(gy, nty - grp * gy);
-    const int64_t r0 = (grp * gy + in % gh) * 128, c0 = (in / gh) * 64;
+    const int64_t r0 = (grp * gy + in % gh) * 128, c0 = (in / gh) * TC;
     const int t = threadIdx.x;
     const int oc = ((t >> 5) << 3) | (t & 7), seg = (t >> 3) & 3;
     float v[32];
@@ -259,19 +297,28 @@ __global__ __launch_bounds__(256) void cast_transposed_kernel(CastArgs a) {
         const uint16_t* x = static_cast<const uint16_t*>(a.x);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int it = t + 256 * j, b = it & 7, m = it >> 3;
-            const int64_t r = r0 + 2 * m, c = c0 + 8 * b;
+            const int it = t + NT * j, cg = it & 7, m = it >> 3;
+            const int64_t r = r0 + 2 * m, c = c0 + 8 * cg;
             uint4 lo = make_uint4(0u, 0u, 0u, 0u), hi = lo;
-            if (c < a.cols) {       // rows are in range: rows % 32 == 0 and the tile band starts below rows
+            if (c < a.cols) {
                 if (r < a.rows) lo = *reinterpret_cast<const uint4*>(x + r * a.ld + c);
                 if (r + 1 < a.rows) hi = *reinterpret_cast<const uint4*>(x + (r + 1) * a.ld + c);
             }
             const uint32_t wl[4] = {lo.x, lo.y, lo.z, lo.w}, wh[4] = {hi.x, hi.y, hi.z, hi.w};
+            if constexpr (DUAL) {
+                float v8[8];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) { v8[2 * k] = bf16lo(wl[k]); v8[2 * k + 1] = bf16hi(wl[k]); }
+                dual_row8<FMT, MODE, BF16>(v8, r, c, u, a);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) { v8[2 * k] = bf16lo(wh[k]); v8[2 * k + 1] = bf16hi(wh[k]); }
+                dual_row8<FMT, MODE, BF16>(v8, r + 1, c, u, a);
+            }
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                // column 8b+2k: low halves of both rows; column 8b+2k+1: high halves
-                tile[pair_word(8 * b + 2 * k, m)] = __builtin_amdgcn_perm(wh[k], wl[k], 0x05040100u);
-                tile[pair_word(8 * b + 2 * k + 1, m)] = __builtin_amdgcn_perm(wh[k], wl[k], 0x07060302u);
+                // column 8cg+2k: low halves of both rows; column 8cg+2k+1: high halves
+                tile[pair_word(8 * cg + 2 * k, m)] = __builtin_amdgcn_perm(wh[k], wl[k], 0x05040100u);
+                tile[pair_word(8 * cg + 2 * k + 1, m)] = __builtin_amdgcn_perm(wh[k], wl[k], 0x07060302u);
             }
         }
         __syncthreads();
@@ -298,6 +345,7 @@ __global__ __launch_bounds__(256) void cast_transposed_kernel(CastArgs a) {
 #pragma unroll
                 for (int k = 0; k < 8; ++k) w[k] = 0.0f;
             }
+            if constexpr (DUAL) dual_row8<FMT, MODE, BF16>(w, r0 + rr, c0 + cc, u, a);
 #pragma unroll
             for (int k = 0; k < 8; ++k) tf[tile_word(rr, cc + k)] = w[k];
         }
@@ -316,7 +364,7 @@ __global__ __launch_bounds__(256) void cast_transposed_kernel(CastArgs a) {
             reinterpret_cast<uint8_t*>(a.scales)[orow * (a.rows / 32) + k0 / 32] = (uint8_t)sc;
         }
     }
-    if (FUSED_AMAX) block_reduce_atomic<256>(cm, a.amax_out);
+    if (FUSED_AMAX) block_reduce_atomic<NT>(cm, a.amax_out);
 }
 
 // ------------------------------------------------------------------ 128x128 weight blocks
@@ -332,8 +380,8 @@ __global__ __launch_bounds__(256) void cast_block128_kernel(CastArgs a) {
     float v[64];
 #pragma unroll
     for (int j = 0; j < 8; ++j) load8<BF16>(src + j * 8 * esz, v + 8 * j);
-    ChunkStats s0 = chunk_stats(v), s1 = chunk_stats(v + 32);
-    uint32_t m = wave_max_u32(max(s0.mx, s1.mx));
+    const uint32_t m0 = chunk_max<32>(v), m1 = chunk_max<32>(v + 32);
+    uint32_t m = wave_max_u32(max(m0, m1));
     __shared__ uint32_t red[4];
     if ((t & 63) == 0) red[t >> 6] = m;
     __syncthreads();
@@ -341,8 +389,8 @@ __global__ __launch_bounds__(256) void cast_block128_kernel(CastArgs a) {
     const float s = scale_from_amax<FMT>(__uint_as_float(bm), 1.0f);
     const float y = recip_rn(s);
     uint32_t out[16];
-    cast32_div<FMT, false>(v, s, y, 0, divisor_ok(s) && dividends_ok(s0.mx, s0.mn), out);
-    cast32_div<FMT, false>(v + 32, s, y, 0, divisor_ok(s) && dividends_ok(s1.mx, s1.mn), out + 8);
+    cast_div<FMT, false, 32>(v, s, y, 0, divisor_ok(s) && dividends_ok(m0, chunk_min_m1<32>(v)), out);
+    cast_div<FMT, false, 32>(v + 32, s, y, 0, divisor_ok(s) && dividends_ok(m1, chunk_min_m1<32>(v + 32)), out + 8);
     uint8_t* dst = a.q + r * a.ldq + c;
     store32(dst, out);
     store32(dst + 32, out + 8);
@@ -448,9 +496,9 @@ static void dispatch_shape(const CastArgs& a, hipStream_t st) {
         if (row_group_ok && a.rows % kmod == 0 && a.cols % 8 == 0) {
             CastArgs b = a;
             if (b.tile_group <= 0) b.tile_group = 8;
-            const int64_t tiles = ((a.cols + 63) / 64) * ((a.rows + 127) / 128);
-            hipLaunchKernelGGL((cast_transposed_kernel<FMT, MODE, BF16, FUSED, DERIVE>), dim3((unsigned)tiles), dim3(256), 0,
-                               st, b);
+            const int64_t tiles = ((a.cols + kTileCols - 1) / kTileCols) * ((a.rows + 127) / 128);
+            hipLaunchKernelGGL((cast_transposed_kernel<FMT, MODE, BF16, FUSED, DERIVE, false>), dim3((unsigned)tiles),
+                               dim3(kTileThreads), 0, st, b);
             return;
         }
     }
@@ -488,6 +536,42 @@ static void dispatch_mode(const CastArgs& a, hipStream_t st) {
         case kModeMX: dispatch_in<FMT, kModeMX>(a, st); break;
         default: dispatch_in<FMT, kModeMoss>(a, st); break;
     }
+}
+
+// ------------------------------------------------------------------ dual cast dispatch
+template <int FMT, int MODE, bool BF16>
+static void dual_flags(const CastArgs& a, hipStream_t st) {
+    CastArgs b = a;
+    if (b.tile_group <= 0) b.tile_group = 8;
+    const int64_t tiles = ((a.cols + kTileCols - 1) / kTileCols) * ((a.rows + 127) / 128);
+    if (tiles == 0) return;
+    const dim3 grid((unsigned)tiles), blk(kTileThreads);
+    const bool derive = a.amax_in != nullptr;
+    const bool fused = a.amax_out != nullptr && MODE == kModeTensor && !derive;
+    if (derive) hipLaunchKernelGGL((cast_transposed_kernel<FMT, MODE, BF16, false, true, true>), grid, blk, 0, st, b);
+    else if (fused) hipLaunchKernelGGL((cast_transposed_kernel<FMT, MODE, BF16, true, false, true>), grid, blk, 0, st, b);
+    else hipLaunchKernelGGL((cast_transposed_kernel<FMT, MODE, BF16, false, false, true>), grid, blk, 0, st, b);
+}
+
+template <int FMT, int MODE>
+static void dual_in(const CastArgs& a, hipStream_t st) {
+    if (a.bf16) dual_flags<FMT, MODE, true>(a, st);
+    else dual_flags<FMT, MODE, false>(a, st);
+}
+
+template <int FMT>
+static void dual_mode(const CastArgs& a, hipStream_t st) {
+    switch (a.mode) {
+        case kModeTensor: dual_in<FMT, kModeTensor>(a, st); break;
+        case kModeMX: dual_in<FMT, kModeMX>(a, st); break;
+        default: dual_in<FMT, kModeMoss>(a, st); break;
+    }
+}
+
+int launch_cast_dual(const CastArgs& a, hipStream_t st) {
+    if (a.fmt == kE4M3) dual_mode<kE4M3>(a, st);
+    else dual_mode<kE5M2>(a, st);
+    return 0;
 }
 
 int launch_cast(const CastArgs& a, hipStream_t st) {

@@ -127,6 +127,29 @@ int fp8_quantize(int mode, int fmt, const void* x, int in_dtype,
                  void* stream);
 
 /*
+ * fp8_quantize_dual -- both quantized copies of one operand in a single pass over it: q (rows x
+ * cols, groups along cols) and qt (cols x rows, groups along rows), byte-for-byte what
+ * fp8_quantize writes with transpose_out = 0 and with transpose_out = 1 under the same tensor
+ * scale.  A linear layer's forward and backward GEMMs need each operand grouped along two
+ * different K axes ([NANO] "实现": the three GEMMs; [MOSS] section 4: S is per source tensor, so
+ * both copies share it).
+ *   mode: FP8Q_TENSOR, FP8Q_MX or FP8Q_MOSS (FP8Q_BLOCK gives FP8Q_ERR_INVALID_ARG).
+ *   q, ldq, scales:     the transpose_out = 0 copy (scales u8[rows][ceil(cols/32)] for MX/MOSS).
+ *   qt, ldqt, scales_t: the transpose_out = 1 copy (scales_t u8[cols][ceil(rows/32)] for MX/MOSS).
+ *   tensor_scale, scale_is_input, amax_out: as in fp8_quantize (current scaling computes the amax
+ *   and the scale once for both copies).
+ * Limits (FP8Q_ERR_UNSUPPORTED otherwise): those of fp8_quantize.  rows % 32 == 0,
+ * cols % 32 == 0, ldq % 16 == 0, ldqt % 16 == 0 and 16-byte aligned q, qt use the one-pass kernel;
+ * other shapes are served by the two single-copy casts.
+ */
+int fp8_quantize_dual(int mode, int fmt, const void* x, int in_dtype,
+                      int64_t rows, int64_t cols, int64_t ld,
+                      uint8_t* q, int64_t ldq, void* scales,
+                      uint8_t* qt, int64_t ldqt, void* scales_t,
+                      float* tensor_scale, int scale_is_input, float* amax_out,
+                      void* stream);
+
+/*
  * fp8_history_update -- delayed-scaling state update ([FLAX] section 2.3), called after the cast
  * of step t with that step's amax a_t:
  *     history <- roll(history, -1) with history[0] = *amax_new   (newest at index 0)
@@ -156,8 +179,9 @@ int fp8_history_update(float* history, int64_t len, const float* amax_new,
  *                scales are applied by the matrix-core instruction ([MOSS] section 1).
  *   FP8Q_MOSS:   as MX, plus Aglobal = &S_A, Bglobal = &S_B applied once in the epilogue as
  *                fl(S_A * S_B) ([MOSS] section 4).
- * Accumulation: each 128-wide K chunk is reduced by the FP8 matrix instruction from zero and its
- * FP32 result is added into an FP32 accumulator (a full-precision accumulation every 128 K).
+ * Accumulation: FP8Q_TENSOR, FP8Q_MX and FP8Q_MOSS keep the whole K sum in the FP8 matrix
+ * instruction's FP32 accumulator; FP8Q_BLOCK reduces each 128-wide K chunk from zero and adds its
+ * scaled FP32 partial into an FP32 accumulator.
  * Limits (FP8Q_ERR_UNSUPPORTED otherwise): K % 16 == 0, lda/ldb % 16 == 0, 16-byte aligned A, B.
  * M, N, K need not be multiples of any tile size.
  */

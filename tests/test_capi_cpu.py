@@ -43,6 +43,13 @@ def test_invalid_arguments(L):
     assert lib.fp8_quantize(0, 0, dummy, 1, 4, 8, 8, 1, 128, 0, dummy, 16, None, None, 1, None, None) == L.ERR_INVALID_ARG
     # alignment / multiples outside the kernels' limits
     assert lib.fp8_quantize(0, 0, dummy, 1, 4, 12, 12, 1, 128, 0, dummy, 16, None, dummy, 1, None, None) == L.ERR_UNSUPPORTED
+    # dual cast: BLOCK is not a dual mode; NULL qt; a derived scale needs amax_out
+    d = lib.fp8_quantize_dual
+    assert d(1, 0, dummy, 1, 32, 32, 32, dummy, 32, dummy, dummy, 32, dummy, dummy, 1, None, None) == L.ERR_INVALID_ARG
+    assert "mode" in _err(L)
+    assert d(2, 0, dummy, 1, 32, 32, 32, dummy, 32, dummy, None, 32, dummy, None, 0, None, None) == L.ERR_INVALID_ARG
+    assert d(3, 0, dummy, 1, 32, 32, 32, dummy, 32, dummy, dummy, 32, dummy, dummy, 0, None, None) == L.ERR_INVALID_ARG
+    assert d(3, 0, dummy, 1, 32, 32, 32, dummy, 16, dummy, dummy, 32, dummy, dummy, 1, None, None) == L.ERR_INVALID_ARG
     # ld smaller than cols
     assert lib.fp8_amax(dummy, 1, 4, 16, 8, dummy, None) == L.ERR_INVALID_ARG
     # history length bounds
