@@ -28,6 +28,7 @@
 // group of output tiles.
 #include "common.cuh"
 #include "gemm_kernel.cuh"
+#include "gemm_pp.cuh"
 #include "kernels.h"
 
 namespace fp8q {
@@ -256,6 +257,20 @@ static void launch_v2(const GemmArgs& g, hipStream_t st) {
     hipLaunchKernelGGL(kern, dim3((unsigned)(ntm * ntn)), dim3(64 * WM * WN), smem, st, g);
 }
 
+// Ping-pong kernel (gemm_pp.cuh): TENSOR, MX and MOSS with K % 128 == 0.
+template <int MODE, int AFMT, int BFMT, bool OUT>
+static void launch_pp(const GemmArgs& g, hipStream_t st) {
+    const int64_t ntm = (g.M + pp::BM - 1) / pp::BM, ntn = (g.N + pp::BN - 1) / pp::BN;
+    auto kern = pp::gemm_pp_kernel<MODE, AFMT, BFMT, OUT>;
+    constexpr size_t smem = pp::lds_bytes<MODE>();
+    static bool attr_set = false;
+    if (!attr_set) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)(ntm * ntn)), dim3(512), smem, st, g);
+}
+
 static bool fits_u32(int64_t bytes) { return bytes >= 0 && bytes < ((int64_t)1 << 32); }
 
 template <int MODE, int AFMT, int BFMT, bool OUT>
@@ -270,10 +285,10 @@ static void launch_sel(const GemmArgs& g, hipStream_t st) {
         // per-128 promotion with the block scales: 256 x 128 tiles, 8 waves of 64 x 64
         launch_v2<MODE, AFMT, BFMT, OUT, 256, 128, 4, 2, 3>(g, st);
     } else {
-        // whole-K accumulation on the matrix cores: 256 x 256 tiles, 8 waves of 64 x 128, when
-        // there are enough tiles to fill the GPU; 128 x 128 tiles otherwise
+        // whole-K accumulation on the matrix cores: the ping-pong kernel's 256 x 256 tiles when
+        // there are enough of them to fill the GPU; 128 x 128 tiles otherwise
         const int64_t big_tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256);
-        if (big_tiles >= 192) launch_v2<MODE, AFMT, BFMT, OUT, 256, 256, 4, 2, 2>(g, st);
+        if (big_tiles >= 192) launch_pp<MODE, AFMT, BFMT, OUT>(g, st);
         else launch_v2<MODE, AFMT, BFMT, OUT, 128, 128, 2, 2, 3>(g, st);
     }
 }

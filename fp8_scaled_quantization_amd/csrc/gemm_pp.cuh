@@ -1,0 +1,349 @@
+// Ping-pong scaled FP8 GEMM for gfx950: 256 x 256 output tiles, 8 waves, two per SIMD.
+//
+// C = dequant(A) . dequant(B)^T with A: M x K and B: N x K, both K-contiguous FP8 bytes, for the
+// schemes whose main loop stays on the matrix cores:
+//   TENSOR  (sum qa*qb) * fl(s_a*s_b) in the epilogue (page "Flax FP8 量化实战指南 ...", section 2.2);
+//   MX      E8M0 scales per 32-wide K group applied by v_mfma_scale_f32_16x16x128_f8f6f4 (page
+//           "MOSS:高效、精确的 FP8 LLM 训练 ...", section 1);
+//   MOSS    as MX, then fl(S_A*S_B) once in the epilogue (same page, section 4).
+//
+// Schedule.  Waves 0-3 (group 0) and waves 4-7 (group 1) each own half of the output tile; each
+// SIMD runs one wave of each group.  A wave alternates a memory phase (issue its share of the
+// global->LDS copies, read its operand fragments and scales from LDS into registers) and a compute
+// phase (32 MFMAs on those fragments), with one workgroup barrier between phases.  Group 1 starts
+// one phase late, so on every SIMD one wave multiplies while the other moves data: the LDS reads
+// never sit between a wave's MFMAs, and the matrix core is fed from both waves in turn.
+//
+// LDS holds two K steps (2 x 64 KiB) and a two-entry ring of scale quads (16 bytes per row = four
+// K steps of E8M0 bytes).  Group 0 reads all of A and B rows 0-127 (B0) of step k in its memory
+// phase (phase 2k).  Group 1 reads B rows 128-255 (B1) of step k in its memory phase (phase 2k+1)
+// but reads A of step k during its compute phase for step k-1 (also phase 2k), one 16-row A block
+// right after the last MFMA that used the previous step's block, so it needs no extra registers.
+// A and B0 of a stage are therefore free one phase after they are first read, and every copy gets
+// about two and a half phases to land:
+//   A, B0 of step k+2 (and the scale quad of a quad's first step)
+//                 group 1, memory phase for step k (phase 2k+1), waited at the end of phase 2k+3;
+//   B1 of step k+1  group 0, memory phase for step k (phase 2k),   waited at the end of phase 2k+2.
+// Copies are issued only in memory phases, interleaved with the fragment reads: a copy instruction
+// can hold its wave while the address unit is busy, which must not delay that wave's MFMAs.
+//
+// Global->LDS copies use buffer_load_dwordx4 ... lds (no VGPR staging; rows past M or N read zero
+// through the buffer range), with each 16-byte chunk c of tile row r stored at chunk position
+// c ^ (r & 7), which keeps both the copy writes and the fragment reads free of bank conflicts.
+#pragma once
+#include "gemm_kernel.cuh"
+
+namespace fp8q {
+namespace pp {
+
+using g2::dma16;
+using g2::lds_addr;
+using g2::make_rsrc;
+using g2::rsrc_t;
+using g2::v4f;
+using g2::v8i;
+
+constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int kA = BM * BK, kB = BN * BK, kStage = kA + kB;   // 64 KiB per K step
+constexpr int kScBase = 2 * kStage;
+constexpr int kScQuad = (BM + BN) * 16;                        // 8 KiB: 4 K steps of E8M0 bytes
+
+template <int MODE>
+constexpr size_t lds_bytes() {
+    return (MODE == kModeMX || MODE == kModeMoss) ? (size_t)(kScBase + 2 * kScQuad) : (size_t)kScBase;
+}
+
+__device__ __forceinline__ void barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// all but the last N vector-memory instructions of this wave complete (they complete in order)
+template <int N>
+__device__ __forceinline__ void wait_vm() { g2::wait_vmcnt<N>(); }
+
+
+__device__ __forceinline__ v8i frag(const uint8_t* row, uint32_t lo, uint32_t hi) {
+    const uint4 a = *reinterpret_cast<const uint4*>(row + lo);
+    const uint4 b = *reinterpret_cast<const uint4*>(row + hi);
+    return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+}
+
+// Block-scaled MFMA whose E8M0 scales sit in byte selA of sa and byte selB of sb (the byte
+// selects must be literals; callers pass loop indices of fully unrolled loops, so the switch folds).
+template <int AF, int BF>
+__device__ __forceinline__ v4f mfma_sel(v8i a, v8i b, v4f c, int sa, int sb, int selA, int selB) {
+#define FP8Q_MF(x, y) \
+    case (x) * 4 + (y): return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, AF, BF, x, sa, y, sb);
+    switch (selA * 4 + selB) {
+        FP8Q_MF(0, 0) FP8Q_MF(0, 1) FP8Q_MF(0, 2) FP8Q_MF(0, 3)
+        FP8Q_MF(1, 0) FP8Q_MF(1, 1) FP8Q_MF(1, 2) FP8Q_MF(1, 3)
+        FP8Q_MF(2, 0) FP8Q_MF(2, 1) FP8Q_MF(2, 2) FP8Q_MF(2, 3)
+        FP8Q_MF(3, 0) FP8Q_MF(3, 1) FP8Q_MF(3, 2)
+        default: break;
+    }
+#undef FP8Q_MF
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, AF, BF, 3, sa, 3, sb);
+}
+
+// One copy instruction: 8 tile rows starting at row r0 (64 rows of scale bytes for a scale quad).
+// The buffer descriptor's range ends at the operand's last row, and the row offset is part of the
+// range-checked per-lane offset, so rows past M or N read zero; the K offset goes into the
+// unchecked scalar offset.  The lane offset is formed by an asm add so that it is recomputed at
+// each copy rather than kept in a register per instruction.
+__device__ __forceinline__ void copy8(uint8_t* lds, rsrc_t rs, uint32_t voff0, uint32_t row_off, uint32_t koff) {
+    uint32_t voff;
+    asm volatile("v_add_u32 %0, %1, %2" : "=v"(voff) : "s"(row_off), "v"(voff0));
+    dma16(lds_addr(lds), rs, voff, koff);
+}
+
+// Group 0, wave wi: A rows 64 wi .. +64 of step s (8 copies).
+__device__ __forceinline__ void copy_A(uint8_t* smem, int s, int wi, rsrc_t ra, uint32_t voffA, uint32_t lda) {
+    uint8_t* st = smem + (s & 1) * kStage;
+    const uint32_t koff = (uint32_t)s * BK;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t r0 = (uint32_t)(wi * 64 + j * 8);
+        copy8(st + r0 * BK, ra, voffA, r0 * lda, koff);
+    }
+}
+// Group 1, wave wi: B rows base + 32 wi .. +32 of step s (4 copies); base 0 (B0) or 128 (B1).
+__device__ __forceinline__ void copy_B(uint8_t* smem, int s, int base, int wi, rsrc_t rb, uint32_t voffB, uint32_t ldb) {
+    uint8_t* st = smem + (s & 1) * kStage + kA;
+    const uint32_t koff = (uint32_t)s * BK;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t r0 = (uint32_t)(base + wi * 32 + j * 8);
+        copy8(st + r0 * BK, rb, voffB, r0 * ldb, koff);
+    }
+}
+// Group 0, wave wi, every fourth step: two instructions of the scale quad for steps s .. s+3.
+__device__ __forceinline__ void copy_quad(uint8_t* smem, int s, int wi, rsrc_t rsa, rsrc_t rsb, uint32_t voffS,
+                                          uint32_t sc_row) {
+    uint8_t* sq = smem + kScBase + ((s >> 2) & 1) * kScQuad;
+    const uint32_t soff = (uint32_t)s * 4;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int inst = wi * 2 + j;              // 0..3: A rows, 4..7: B rows, 64 rows each
+        const uint32_t r0 = (uint32_t)(inst & 3) * 64;
+        copy8(sq + inst * 64 * 16, inst < 4 ? rsa : rsb, voffS, r0 * sc_row, soff);
+    }
+}
+
+template <int MODE, int AFMT, int BFMT, bool OUT_BF16>
+__global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
+    constexpr bool SCALED = MODE == kModeMX || MODE == kModeMoss;
+    static_assert(MODE != kModeBlock, "block scaling promotes per K step; it has its own kernel");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform: kept in SGPRs
+    const int grp = wave >> 2;
+    const int wm = wave & 3, wn = grp;            // wave tile: rows 64 wm .. +64, cols 128 wn .. +128
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int64_t M = g.M, N = g.N;
+    const int64_t ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
+
+    // tile coordinates: undo the round-robin XCD dispatch, then walk groups of 8 tile-rows
+    int64_t b = blockIdx.x;
+    {
+        const int64_t nb = ntm * ntn;
+        if (nb % 8 == 0) b = (b % 8) * (nb / 8) + b / 8;
+    }
+    const int64_t per_group = 8 * ntn;
+    const int64_t gi = b / per_group, first_m = gi * 8;
+    const int64_t gm = min(ntm - first_m, (int64_t)8);
+    const int64_t in_grp = b - gi * per_group;
+    const int64_t m0 = (first_m + in_grp % gm) * BM, n0 = (in_grp / gm) * BN;
+    const int nk = (int)(g.K / BK);
+
+    const int64_t sc_row = 4 * (int64_t)nk;      // E8M0 bytes per row
+    const rsrc_t ra = make_rsrc(g.A + m0 * g.lda, (uint32_t)(max((int64_t)0, M - m0) * g.lda));
+    const rsrc_t rb = make_rsrc(g.B + n0 * g.ldb, (uint32_t)(max((int64_t)0, N - n0) * g.ldb));
+    rsrc_t rsa = rsrc_t{0u, 0u, 0u, 0u}, rsb = rsrc_t{0u, 0u, 0u, 0u};
+    if (SCALED) {
+        rsa = make_rsrc(static_cast<const uint8_t*>(g.Ascale) + m0 * sc_row, (uint32_t)(max((int64_t)0, M - m0) * sc_row));
+        rsb = make_rsrc(static_cast<const uint8_t*>(g.Bscale) + n0 * sc_row, (uint32_t)(max((int64_t)0, N - n0) * sc_row));
+    }
+    // copy lanes: lane i of a copy instruction covers row r0 + i/8 at LDS chunk i%8, fetching global
+    // chunk (i%8) ^ (row & 7) (r0 is a multiple of 8); scale quads take one row per lane
+    const uint32_t ch = (uint32_t)(((lane & 7) ^ ((lane >> 3) & 7)) << 4);
+    const uint32_t voffA = (uint32_t)((lane >> 3) * g.lda) + ch;
+    const uint32_t voffB = (uint32_t)((lane >> 3) * g.ldb) + ch;
+    const uint32_t voffS = (uint32_t)(lane * sc_row);
+    const uint32_t ulda = (uint32_t)g.lda, uldb = (uint32_t)g.ldb, usc = (uint32_t)sc_row;
+    const int wi = wave & 3;
+
+    // fragment read offsets (loop invariant): row base of each 16-row subtile, swizzled chunks
+    const uint32_t cLo = (uint32_t)((g4 ^ (r16 & 7)) << 4), cHi = (uint32_t)(((4 + g4) ^ (r16 & 7)) << 4);
+    const uint32_t rowA = (uint32_t)((wm * 64 + r16) * BK), rowB = (uint32_t)((wn * 128 + r16) * BK);
+
+    v4f acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // ---- prologue: group 1 sends all of step 0 but B1, plus A and B0 of step 1; group 0 sends B1
+    // of step 0 (it sends B1 of step k+1 in its memory phase for step k)
+    if (grp == 0) {
+        copy_B(smem, 0, 128, wi, rb, voffB, uldb);
+        wait_vm0();
+    } else {
+        copy_A(smem, 0, wi, ra, voffA, ulda);
+        copy_B(smem, 0, 0, wi, rb, voffB, uldb);
+        if (SCALED) copy_quad(smem, 0, wi, rsa, rsb, voffS, usc);
+        if (nk > 1) {
+            copy_A(smem, 1, wi, ra, voffA, ulda);
+            copy_B(smem, 1, 0, wi, rb, voffB, uldb);
+            wait_vm<12>();
+        } else {
+            wait_vm0();
+        }
+    }
+    barrier();
+    v8i fa[4], fb[8];
+    if (grp == 1) {
+        // group 1 reads A of step 0 while group 0 has its first memory phase
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = frag(smem + rowA + i * 16 * BK, cLo, cHi);
+        barrier();
+    }
+
+    int sca = 0, scb0 = 0, scb1 = 0;
+    for (int k = 0; k < nk; ++k) {
+        // ---- memory phase: scale words first, then fragment reads interleaved with this phase's
+        // copies (a copy may wait for the address unit; the LDS reads queued around it keep going)
+        uint32_t sw[12];
+        if (SCALED) {
+            const uint32_t* sq = reinterpret_cast<const uint32_t*>(smem + kScBase + ((k >> 2) & 1) * kScQuad);
+            const int qs = k & 3;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sw[i] = sq[(wm * 64 + i * 16 + r16) * 4 + qs];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sw[4 + j] = sq[(BM + wn * 128 + j * 16 + r16) * 4 + qs];
+        }
+        {
+            const uint8_t* sa = smem + (k & 1) * kStage;
+            const uint8_t* sb = sa + kA;
+            if (grp == 0) {
+                // A and B0 of step k; B1 of step k+1 (4 copies), one per three fragment reads
+                const bool cp = k + 1 < nk;
+                uint8_t* st = smem + ((k + 1) & 1) * kStage + kA;
+                const uint32_t koff = (uint32_t)(k + 1) * BK;
+#pragma unroll
+                for (int q = 0; q < 12; ++q) {
+                    if (cp && q % 3 == 0) {
+                        const uint32_t r0 = (uint32_t)(128 + wi * 32 + (q / 3) * 8);
+                        copy8(st + r0 * BK, rb, voffB, r0 * uldb, koff);
+                    }
+                    if (q < 4) fa[q] = frag(sa + rowA + q * 16 * BK, cLo, cHi);
+                    else fb[q - 4] = frag(sb + rowB + (q - 4) * 16 * BK, cLo, cHi);
+                }
+                // B1 of step k (sent one memory phase ago) lands before group 1 reads it next phase
+                if (cp) wait_vm<4>();
+                else wait_vm0();
+            } else {
+                // B1 of step k; A and B0 of step k+2 (8 + 4 copies) and the scale quad
+                const bool cp = k + 2 < nk;
+                uint8_t* st = smem + (k & 1) * kStage;
+                const uint32_t koff = (uint32_t)(k + 2) * BK;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    if (cp) {
+#pragma unroll
+                        for (int c = (q < 4 ? 2 * q : q + 4); c < (q < 4 ? 2 * q + 2 : q + 5); ++c) {
+                            if (c < 8) {
+                                const uint32_t r0 = (uint32_t)(wi * 64 + c * 8);
+                                copy8(st + r0 * BK, ra, voffA, r0 * ulda, koff);
+                            } else {
+                                const uint32_t r0 = (uint32_t)(wi * 32 + (c - 8) * 8);
+                                copy8(st + kA + r0 * BK, rb, voffB, r0 * uldb, koff);
+                            }
+                        }
+                    }
+                    fb[q] = frag(sb + rowB + q * 16 * BK, cLo, cHi);
+                }
+                const bool quad = SCALED && cp && ((k + 2) & 3) == 0;
+                if (quad) copy_quad(smem, k + 2, wi, rsa, rsb, voffS, usc);
+                // A and B0 of step k+1 (sent one memory phase ago) land before group 0 reads them
+                // next phase; this phase's copies may stay in flight
+                if (quad) wait_vm<14>();
+                else if (cp) wait_vm<12>();
+                else wait_vm0();
+            }
+        }
+        if (SCALED) {
+            // byte g4 of a row's word = the E8M0 scale of (row, group g4) for this step; four
+            // subtiles per register, picked in the MFMA by its byte select
+            const int sh = 8 * g4;
+            uint32_t pa = 0, pb0 = 0, pb1 = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pa |= ((sw[i] >> sh) & 0xFFu) << (8 * i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pb0 |= ((sw[4 + j] >> sh) & 0xFFu) << (8 * j);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pb1 |= ((sw[8 + j] >> sh) & 0xFFu) << (8 * j);
+            sca = (int)pa;
+            scb0 = (int)pb0;
+            scb1 = (int)pb1;
+            // finish the packing here, in the memory phase, not after the barrier
+            asm volatile("" ::"v"(sca), "v"(scb0), "v"(scb1));
+        }
+        wait_lgkm0();
+        barrier();
+        // ---- compute phase (group 1 also reads A of step k+1, row block by row block)
+        const bool next_a = grp == 1 && k + 1 < nk;
+        const uint8_t* sn = smem + ((k + 1) & 1) * kStage;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (SCALED)
+                    acc[i][j] = mfma_sel<AFMT, BFMT>(fa[i], fb[j], acc[i][j], sca, j < 4 ? scb0 : scb1, i, j & 3);
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[i], fb[j], acc[i][j], AFMT, BFMT, 0, 0,
+                                                                                  0, 0);
+            }
+            if (next_a) {
+                // the eight MFMAs above are issued before fa[i] is overwritten
+                asm volatile("" ::"v"(acc[i][0]), "v"(acc[i][1]), "v"(acc[i][2]), "v"(acc[i][3]), "v"(acc[i][4]),
+                             "v"(acc[i][5]), "v"(acc[i][6]), "v"(acc[i][7]));
+                fa[i] = frag(sn + rowA + i * 16 * BK, cLo, cHi);
+            }
+        }
+        // every accumulator is read here, so all 32 MFMAs are issued before the barrier
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            asm volatile("" ::"v"(acc[i][0]), "v"(acc[i][1]), "v"(acc[i][2]), "v"(acc[i][3]), "v"(acc[i][4]),
+                         "v"(acc[i][5]), "v"(acc[i][6]), "v"(acc[i][7]));
+        barrier();
+    }
+    if (grp == 0) barrier();          // matches group 1's extra barrier at the start
+
+    // ---- epilogue
+    float f = 1.0f;
+    if (MODE == kModeTensor || MODE == kModeMoss) f = (*g.Aglobal) * (*g.Bglobal);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t col = n0 + wn * 128 + j * 16 + r16;
+            if (col >= N) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t row = m0 + wm * 64 + i * 16 + 4 * g4 + e;
+                if (row < M) {
+                    const float v = (MODE == kModeTensor || MODE == kModeMoss) ? acc[i][j][e] * f : acc[i][j][e];
+                    if (OUT_BF16) static_cast<uint16_t*>(g.C)[row * g.ldc + col] = g2::f32_to_bf16_rne(v);
+                    else static_cast<float*>(g.C)[row * g.ldc + col] = v;
+                }
+            }
+        }
+    }
+}
+
+}  // namespace pp
+}  // namespace fp8q

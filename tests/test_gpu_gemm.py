@@ -168,6 +168,25 @@ def test_gemm_moss_forward_backward_full_size_sampled(fq, orc):
                    4096, 4096, 16384, 53, "moss dW")
 
 
+# Shapes with enough 256 x 256 tiles (>= 192) to take the ping-pong kernel, with partial tiles in
+# M and N and K of one, two and five 128-wide steps (the copy pipeline's start-up and drain cases).
+PINGPONG = [(3000, 4000, 128), (3000, 4000, 256), (2900, 4100, 640)]
+
+
+@pytest.mark.parametrize("mode", [TENSOR, MX, MOSS])
+@pytest.mark.parametrize("M,N,K", PINGPONG)
+@pytest.mark.parametrize("fmts", [(E4M3, E4M3), (E5M2, E4M3)])
+def test_gemm_pingpong_ragged_sampled(fq, orc, mode, M, N, K, fmts):
+    afmt, bfmt = fmts
+    xa = workloads.random_matrix(M + 7 * K, M, K, 2.0)
+    xb = workloads.random_matrix(N + 11 * K, N, K, 0.05)
+    A, (hqa, hsa, hga) = _quant_operand(fq, orc, xa, mode, afmt, None)
+    B, (hqb, hsb, hgb) = _quant_operand(fq, orc, xb, mode, bfmt, None)
+    _sampled_check(fq, orc, mode, A, afmt, B, bfmt, _rows_deq(orc, mode, hqa, hsa, hga, afmt, None),
+                   _rows_deq(orc, mode, hqb, hsb, hgb, bfmt, None), M, N, K, M + N + K,
+                   "pingpong mode %d %dx%dx%d" % (mode, M, N, K))
+
+
 def test_gemm_determinism_and_k_zero(fq, orc):
     xa = workloads.random_matrix(1, 256, 512)
     xb = workloads.random_matrix(2, 192, 512)
