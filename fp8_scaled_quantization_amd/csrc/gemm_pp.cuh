@@ -65,6 +65,16 @@ template <int N>
 __device__ __forceinline__ void wait_vm() { g2::wait_vmcnt<N>(); }
 
 
+// (a & m) | (b & ~m)
+__device__ __forceinline__ uint32_t bitsel(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// two fp32 -> packed bf16 (round to nearest even; v_cvt_pk_bf16_f32), a in the low half
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 __device__ __forceinline__ v8i frag(const uint8_t* row, uint32_t lo, uint32_t hi) {
     const uint4 a = *reinterpret_cast<const uint4*>(row + lo);
     const uint4 b = *reinterpret_cast<const uint4*>(row + hi);
@@ -158,6 +168,13 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
     const int64_t in_grp = b - gi * per_group;
     const int64_t m0 = (first_m + in_grp % gm) * BM, n0 = (in_grp / gm) * BN;
     const int nk = (int)(g.K / BK);
+    // global dequantisation factors (TENSOR: s_a, s_b; MOSS: S_A, S_B), read early through the
+    // scalar cache; their product fl(s_a * s_b) scales the accumulators in the epilogue
+    float ga = 1.0f, gb = 1.0f;
+    if (MODE == kModeTensor || MODE == kModeMoss) {
+        ga = g2::load_uniform_f32(g.Aglobal);
+        gb = g2::load_uniform_f32(g.Bglobal);
+    }
 
     const int64_t sc_row = 4 * (int64_t)nk;      // E8M0 bytes per row
     const rsrc_t ra = make_rsrc(g.A + m0 * g.lda, (uint32_t)(max((int64_t)0, M - m0) * g.lda));
@@ -324,21 +341,53 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
     if (grp == 0) barrier();          // matches group 1's extra barrier at the start
 
     // ---- epilogue
-    float f = 1.0f;
-    if (MODE == kModeTensor || MODE == kModeMoss) f = (*g.Aglobal) * (*g.Bglobal);
+    const float f = (MODE == kModeTensor || MODE == kModeMoss) ? ga * gb : 1.0f;
+    if (OUT_BF16 && m0 + BM <= M && n0 + BN <= N) {
+        // Full tile.  A 4x4 transpose of bf16 values within each quad of lanes turns the MFMA
+        // layout (lane r16 holds one column, four rows) into one row and four columns per lane:
+        // lane (g4, r16 = 4 c4 + q) then holds row 4 g4 + q, columns 4 c4 .. 4 c4 + 3 of a 16 x 16
+        // subtile, stored with one 8-byte write (each row's 32 bytes come from four lanes).
+        const int q = r16 & 3, c4 = r16 >> 2;
+        // lane-constant masks (all ones for odd q / for q >= 2): selections are bit selects,
+        // not branches
+        const uint32_t modd = 0u - (uint32_t)(q & 1), mhi = 0u - (uint32_t)(q >> 1);
+        uint16_t* const cw = static_cast<uint16_t*>(g.C) + (m0 + wm * 64) * g.ldc + n0 + wn * 128;
+        const uint32_t loff = (uint32_t)((4 * g4 + q) * g.ldc + 4 * c4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i) {
+            uint16_t* const ci = cw + (int64_t)i * 16 * g.ldc;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t col = n0 + wn * 128 + j * 16 + r16;
-            if (col >= N) continue;
+            for (int j = 0; j < 8; ++j) {
+                const v4f v = acc[i][j] * f;
+                const uint32_t w0 = pack_bf16(v[0], v[1]), w1 = pack_bf16(v[2], v[3]);   // rows (0,1), (2,3)
+                // swap with lane q^1: even lanes collect rows 0 and 2, odd lanes rows 1 and 3, of
+                // two adjacent columns
+                const uint32_t s1 = bitsel(modd, (w0 & 0xFFFFu) | (w1 << 16), (w0 >> 16) | (w1 & 0xFFFF0000u));
+                const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s1, 0xB1, 0xF, 0xF, false);   // [1,0,3,2]
+                const uint32_t x0 = bitsel(modd, (r1 & 0xFFFFu) | (w0 & 0xFFFF0000u), (w0 & 0xFFFFu) | (r1 << 16));
+                const uint32_t x1 = bitsel(modd, (r1 >> 16) | (w1 & 0xFFFF0000u), (w1 & 0xFFFFu) | (r1 & 0xFFFF0000u));
+                // swap with lane q^2: lane q ends with row q, columns 0-1 and 2-3 of the quad
+                const uint32_t r2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)bitsel(mhi, x0, x1), 0x4E, 0xF, 0xF, false);   // [2,3,0,1]
+                const uint2 d = make_uint2(bitsel(mhi, r2, x0), bitsel(mhi, x1, r2));
+                *reinterpret_cast<uint2*>(ci + loff + j * 16) = d;
+            }
+        }
+    } else {
+        // partial tile or fp32 output: element by element, masked
+        const int64_t row0 = m0 + wm * 64 + 4 * g4, col0 = n0 + wn * 128 + r16;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t row = m0 + wm * 64 + i * 16 + 4 * g4 + e;
-                if (row < M) {
-                    const float v = (MODE == kModeTensor || MODE == kModeMoss) ? acc[i][j][e] * f : acc[i][j][e];
-                    if (OUT_BF16) static_cast<uint16_t*>(g.C)[row * g.ldc + col] = g2::f32_to_bf16_rne(v);
-                    else static_cast<float*>(g.C)[row * g.ldc + col] = v;
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int64_t col = col0 + j * 16;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t row = row0 + i * 16 + e;
+                    if (row < M && col < N) {
+                        const float v = acc[i][j][e] * f;
+                        if (OUT_BF16) static_cast<uint16_t*>(g.C)[row * g.ldc + col] = g2::f32_to_bf16_rne(v);
+                        else static_cast<float*>(g.C)[row * g.ldc + col] = v;
+                    }
                 }
             }
         }
