@@ -19,14 +19,21 @@
  *          cast after a clamp to +-max).
  *  [HF]    "Transformers 中的细粒度 FP8 量化配置、DeepGEMM 加速路径与 UE8M0 缩放格式完全指南",
  *          section 一 (128x128 weight blocks, per-token groups of 128 along the input channels,
- *          weight_scale_inv of shape (ceil(out/128), ceil(in/128))), section 七 (UE8M0 scales).
+ *          weight_scale_inv of shape (ceil(out/128), ceil(in/128))), section 四 (static activation
+ *          scheme: one supplied per-tensor activation scale), section 五 (dequantize: the block
+ *          scale folded back into the weight, bf16 result), section 七 (UE8M0 block scales: one
+ *          power-of-two byte per block; power-of-two scales stored in fp32 containers converted
+ *          exactly; rounding fp32 scales up to UE8M0 without re-quantizing corrupts the output).
  *  [MOSS]  "MOSS:高效、精确的 FP8 LLM 训练,采用微尺度和自动尺度变换",
  *          section 1 (MXFP8: groups of 32 consecutive values, power-of-two shared scale from the
  *                     group's max, divide, store FP8),
  *          section 2 (SNR as signal power over quantization-noise power, in dB),
  *          section 4 (two-level scaling, steps 1-4: per-32 float scale, global factor = max of
  *                     them, E8M0 local factor in (0,1], effective scale = global * local,
- *                     FP32 factors applied once in the epilogue).
+ *                     FP32 factors applied once in the epilogue),
+ *          section 5 (automatic weight scaling: the weight max grows by at most the learning
+ *                     rate per step, so the scale is predicted from the last measured max plus
+ *                     the learning rates since, and re-measured at the end of each interval).
  *
  * Readings where the pages leave a step open are listed in the design notes; the ones that
  * change arithmetic here are:
@@ -38,7 +45,11 @@
  *  - MX exponent: the smallest e in [-127,127] with MAX*2^e >= amax (127 if none);
  *  - MOSS local exponent: the smallest e in [-127,0] with S*2^e >= s_i (0 if none); the
  *    element is fl(fl(x/S) * 2^-e), clipped, rounded;
- *  - E8M0 byte = e + 127.
+ *  - E8M0 byte = e + 127;
+ *  - UE8M0 block scale: the MX exponent rule applied to a whole 2-D block;
+ *  - automatic scaling: predicted max = fl(base + sum of the learning rates since the last
+ *    measurement) in fp32 (the sum accumulated in fp32 step by step);
+ *  - merging two branches' updated history/scale pairs takes the elementwise max.
  */
 #include <math.h>
 #include <stdint.h>
@@ -53,6 +64,7 @@
 #define ORC_BLOCK 1
 #define ORC_MX 2
 #define ORC_MOSS 3
+#define ORC_BLOCK_E8M0 4
 
 /* ---------------------------------------------------------------- formats ---- */
 
@@ -231,6 +243,60 @@ void orc_quantize_block(const void* x, int in_kind, int64_t rows, int64_t cols, 
 }
 
 /* Smallest e in [lo, hi] with base * 2^e >= target (products exact in double); hi if none. */
+static int smallest_pow2_exponent(double base, double target, int lo, int hi);
+
+/* UE8M0 block scaling: one power-of-two scale 2^e per (br x bc) block, e = smallest integer in
+ * [-127, 127] with MAX * 2^e >= amax_block (127 if none), stored as the byte e + 127 in
+ * e8m0[ceil(R/br)][ceil(C/bc)]; element encode(clip(fl(x * 2^-e))) (exact scaling, so nothing
+ * clips unless the block holds non-finite values).  [HF] section 七 */
+void orc_quantize_block_e8m0(const void* x, int in_kind, int64_t rows, int64_t cols, int64_t ld, int fmt,
+                             int64_t br, int64_t bc, int transpose, uint8_t* q, int64_t ldq, uint8_t* e8m0) {
+    int64_t R, C;
+    float* t = logical_f32(x, in_kind, rows, cols, ld, transpose, &R, &C);
+    int64_t nbr = (R + br - 1) / br, nbc = (C + bc - 1) / bc;
+    #pragma omp parallel for schedule(static)
+    for (int64_t bi = 0; bi < nbr; ++bi) {
+        for (int64_t bj = 0; bj < nbc; ++bj) {
+            int64_t r0 = bi * br, r1 = r0 + br < R ? r0 + br : R;
+            int64_t c0 = bj * bc, c1 = c0 + bc < C ? c0 + bc : C;
+            float am = amax_f32(t, C, r0, r1, c0, c1);
+            int e = smallest_pow2_exponent(orc_fp8_max(fmt), (double)am, -127, 127);
+            e8m0[bi * nbc + bj] = (uint8_t)(e + 127);
+            float f = (float)ldexp(1.0, -e);
+            for (int64_t r = r0; r < r1; ++r)
+                for (int64_t c = c0; c < c1; ++c)
+                    q[r * ldq + c] = orc_fp8_encode(clip_max(t[r * C + c] * f, fmt), fmt);
+        }
+    }
+    free(t);
+}
+
+/* Exact conversion of power-of-two scales held in fp32 to UE8M0 bytes: 2^e with e in [-127, 127]
+ * becomes e + 127.  Any other value (not a power of two, zero, negative, non-finite, out of range)
+ * cannot be represented exactly; it gets the byte 0xFF and is counted.  Returns that count.
+ * [HF] section 七 (checkpoints that keep power-of-two UE8M0 scales in fp32 containers are converted
+ * exactly on load) */
+int64_t orc_scales_f32_to_e8m0(const float* s, int64_t n, uint8_t* out) {
+    int64_t bad = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        double v = (double)s[i];
+        int ok = 0;
+        if (v > 0.0 && !isinf(v) && !isnan(v)) {
+            int ex;
+            double m = frexp(v, &ex);                 /* v = m * 2^ex, m in [0.5, 1) */
+            if (m == 0.5 && ex - 1 >= -127 && ex - 1 <= 127) {
+                out[i] = (uint8_t)(ex - 1 + 127);
+                ok = 1;
+            }
+        }
+        if (!ok) {
+            out[i] = 0xFF;
+            ++bad;
+        }
+    }
+    return bad;
+}
+
 static int smallest_pow2_exponent(double base, double target, int lo, int hi) {
     for (int e = lo; e <= hi; ++e)
         if (base * ldexp(1.0, e) >= target) return e;
@@ -326,11 +392,42 @@ void orc_delayed_step(const void* x, int in_kind, int64_t rows, int64_t cols, in
     if (amax_out) *amax_out = a;
 }
 
+/* Two uses of one delayed-scaling state (branches, micro-batches) each produce an updated
+ * history and scale; they are combined by taking the larger value, element by element, not by
+ * adding them (lax.max semantics: NaN propagates).  dst <- max(dst, src).  [FLAX] section 5.3 */
+static float max_nan(float a, float b) {
+    if (isnan(a) || isnan(b)) return NAN;
+    return a > b ? a : b;
+}
+void orc_history_merge(float* hist_dst, const float* hist_src, int64_t len, float* scale_dst, float scale_src) {
+    for (int64_t i = 0; i < len; ++i) hist_dst[i] = max_nan(hist_dst[i], hist_src[i]);
+    *scale_dst = max_nan(*scale_dst, scale_src);
+}
+
+/* Automatic weight scaling, one step.  state[0] = base (the weight max measured at the start of
+ * the current interval), state[1] = the sum of the learning rates applied since.  On a rescale
+ * step (the interval's first) base <- amax_now (a fresh max-reduction of the weight) and the sum
+ * restarts at 0.  The step's scale is fl(fl(base + sum) / MAX) (1.0 if that max is zero or
+ * non-finite); then this step's learning rate is added to the sum.  The prediction is an upper
+ * bound because each optimizer step moves a weight by at most the learning rate.
+ * [MOSS] section 5 */
+float orc_auto_scale_step(float* state, int rescale, float amax_now, float lr, int fmt) {
+    if (rescale) {
+        state[0] = amax_now;
+        state[1] = 0.0f;
+    }
+    float predicted = state[0] + state[1];
+    float s = orc_compute_scale(predicted, fmt, 1.0f);
+    state[1] = state[1] + lr;
+    return s;
+}
+
 /* ---------------------------------------------------------------- dequant ---- */
 
 /* Dequantize one K-contiguous operand (rows x K) into fp64: q * scale, exact in double.
  * TENSOR: scale = *global.  BLOCK: fp32 scale per (br x bc) block, [ceil(rows/br)][K/bc].
- * MX: 2^(byte-127) per (row, 32-group).  MOSS: as MX times *global. */
+ * BLOCK_E8M0: 2^(byte-127) per (br x bc) block.  MX: 2^(byte-127) per (row, 32-group).
+ * MOSS: as MX times *global. */
 void orc_dequantize(int mode, const uint8_t* q, int fmt, int64_t rows, int64_t K, int64_t ldq,
                     const void* scales, int64_t br, int64_t bc, const float* global, double* out) {
     int64_t ng = (K + 31) / 32, nbc = bc > 0 ? (K + bc - 1) / bc : 0;
@@ -340,11 +437,43 @@ void orc_dequantize(int mode, const uint8_t* q, int fmt, int64_t rows, int64_t K
             double v = orc_fp8_decode(q[r * ldq + k], fmt), s;
             if (mode == ORC_TENSOR) s = (double)*global;
             else if (mode == ORC_BLOCK) s = (double)((const float*)scales)[(r / br) * nbc + k / bc];
+            else if (mode == ORC_BLOCK_E8M0)
+                s = ldexp(1.0, (int)((const uint8_t*)scales)[(r / br) * nbc + k / bc] - 127);
             else {
                 s = ldexp(1.0, (int)((const uint8_t*)scales)[r * ng + k / 32] - 127);
                 if (mode == ORC_MOSS) s *= (double)*global;
             }
             out[r * K + k] = v * s;
+        }
+}
+
+/* fp32 -> bf16 bits, round to nearest even (NaN -> quiet NaN with the sign kept). */
+static uint16_t bf16_rne(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7FFFu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+/* Block dequantize of a (rows x K) FP8 weight: out[r][k] = fl(decode(q) * s_block) as fp32, or
+ * that fp32 product rounded to bf16 (out_bf16 = 1; out is then uint16 bit patterns).  The block
+ * scale is fp32 (BLOCK) or 2^(byte-127) (BLOCK_E8M0), [ceil(rows/br)][ceil(K/bc)].
+ * [HF] section 五 (the block scale folded into the weight, bf16 result) */
+void orc_block_dequantize(int mode, const uint8_t* q, int fmt, int64_t rows, int64_t K, int64_t ldq,
+                          const void* scales, int64_t br, int64_t bc, int out_bf16, void* out) {
+    int64_t nbc = (K + bc - 1) / bc;
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t k = 0; k < K; ++k) {
+            float v = (float)orc_fp8_decode(q[r * ldq + k], fmt);    /* exact in fp32 */
+            int64_t bi = (r / br) * nbc + k / bc;
+            float s = mode == ORC_BLOCK_E8M0 ? (float)ldexp(1.0, (int)((const uint8_t*)scales)[bi] - 127)
+                                             : ((const float*)scales)[bi];
+            float p = v * s;                                        /* one fp32 rounding */
+            if (out_bf16) ((uint16_t*)out)[r * K + k] = bf16_rne(p);
+            else ((float*)out)[r * K + k] = p;
         }
 }
 

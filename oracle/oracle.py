@@ -18,7 +18,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 E4M3, E5M2 = 0, 1
 IN_F32, IN_BF16 = 0, 1
-TENSOR, BLOCK, MX, MOSS = 0, 1, 2, 3
+TENSOR, BLOCK, MX, MOSS, BLOCK_E8M0 = 0, 1, 2, 3, 4
 FP8_MAX = {E4M3: 448.0, E5M2: 57344.0}
 
 _lib = None
@@ -61,6 +61,11 @@ def lib():
             "orc_dequantize": (None, [I, P, I, I64, I64, I64, P, I64, I64, P, P]),
             "orc_gemm_ref": (None, [P, P, I64, I64, I64, P, I64, P, P]),
             "orc_snr_db": (D, [P, P, I64]),
+            "orc_quantize_block_e8m0": (None, [P, I, I64, I64, I64, I, I64, I64, I, P, I64, P]),
+            "orc_scales_f32_to_e8m0": (I64, [P, I64, P]),
+            "orc_history_merge": (None, [P, P, I64, P, F]),
+            "orc_auto_scale_step": (F, [P, I, F, F, I]),
+            "orc_block_dequantize": (None, [I, P, I, I64, I64, I64, P, I64, I64, I, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -157,6 +162,25 @@ def quantize_block(x: np.ndarray, fmt: int, br: int, bc: int, transpose: bool = 
     return q, s
 
 
+def quantize_block_e8m0(x: np.ndarray, fmt: int, br: int, bc: int, transpose: bool = False):
+    """UE8M0 block scaling: (q, e8m0 bytes [ceil(R/br)][ceil(C/bc)])."""
+    x, kind = _input(x)
+    R, C = _out_shape(x, transpose)
+    q = np.empty((R, C), np.uint8)
+    e = np.empty((-(-R // br), -(-C // bc)), np.uint8)
+    lib().orc_quantize_block_e8m0(_p(x), kind, x.shape[0], x.shape[1], x.shape[1], fmt, br, bc, int(transpose),
+                                  _p(q), C, _p(e))
+    return q, e
+
+
+def scales_f32_to_e8m0(s: np.ndarray):
+    """Exact fp32 -> UE8M0 conversion of power-of-two scales: (bytes, count of inexact entries)."""
+    s = np.ascontiguousarray(s, np.float32)
+    out = np.empty(s.shape, np.uint8)
+    bad = lib().orc_scales_f32_to_e8m0(_p(s), s.size, _p(out))
+    return out, int(bad)
+
+
 def quantize_mx(x: np.ndarray, fmt: int, transpose: bool = False):
     x, kind = _input(x)
     R, C = _out_shape(x, transpose)
@@ -213,6 +237,20 @@ def delayed_step(x: np.ndarray, fmt: int, scale: np.ndarray, hist: np.ndarray, t
     return q, a[0]
 
 
+def history_merge(hist_dst: np.ndarray, scale_dst: np.ndarray, hist_src: np.ndarray, scale_src: float) -> None:
+    """Combine two branches' updated (history, scale) by elementwise max, in place in *_dst."""
+    assert hist_dst.dtype == np.float32 and scale_dst.dtype == np.float32 and hist_dst.flags.c_contiguous
+    hs = np.ascontiguousarray(hist_src, np.float32)
+    assert hs.size == hist_dst.size
+    lib().orc_history_merge(_p(hist_dst), _p(hs), hist_dst.size, _p(scale_dst), float(scale_src))
+
+
+def auto_scale_step(state: np.ndarray, rescale: bool, amax_now: float, lr: float, fmt: int) -> np.float32:
+    """One automatic-scaling step; `state` (fp32[2]: base, learning-rate sum) is updated in place."""
+    assert state.dtype == np.float32 and state.size == 2 and state.flags.c_contiguous
+    return np.float32(lib().orc_auto_scale_step(_p(state), int(bool(rescale)), float(amax_now), float(lr), fmt))
+
+
 # ------------------------------------------------------------------ dequant / GEMM / SNR
 def dequantize(mode: int, q: np.ndarray, fmt: int, scales=None, global_scale=None,
                block=(1, 128)) -> np.ndarray:
@@ -223,11 +261,21 @@ def dequantize(mode: int, q: np.ndarray, fmt: int, scales=None, global_scale=Non
     g = np.array([1.0 if global_scale is None else global_scale], np.float32)
     if mode == BLOCK:
         sc = np.ascontiguousarray(scales, np.float32)
-    elif mode in (MX, MOSS):
+    elif mode in (MX, MOSS, BLOCK_E8M0):
         sc = np.ascontiguousarray(scales, np.uint8)
     else:
         sc = np.zeros(1, np.float32)
     lib().orc_dequantize(mode, _p(q), fmt, rows, K, K, _p(sc), block[0], block[1], _p(g), _p(out))
+    return out
+
+
+def block_dequantize(mode: int, q: np.ndarray, fmt: int, scales: np.ndarray, block=(128, 128), out_bf16: bool = True):
+    """fl32(decode(q) * block scale), optionally rounded to bf16 (returned as uint16 bit patterns)."""
+    q = np.ascontiguousarray(q, np.uint8)
+    rows, K = q.shape
+    sc = np.ascontiguousarray(scales, np.uint8 if mode == BLOCK_E8M0 else np.float32)
+    out = np.empty((rows, K), np.uint16 if out_bf16 else np.float32)
+    lib().orc_block_dequantize(mode, _p(q), fmt, rows, K, K, _p(sc), block[0], block[1], int(bool(out_bf16)), _p(out))
     return out
 
 

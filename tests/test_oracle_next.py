@@ -1,0 +1,234 @@
+"""Pins for the oracle's next-step functions: merging delayed-scaling state across branches, MOSS
+automatic weight scaling, UE8M0 (power-of-two) 128x128 block scales, the exact fp32 -> UE8M0 scale
+conversion, and block dequantization.  Each is checked against what the pages or the mathematics
+fix: the Flax page's worked example, the upper-bound property the MOSS page derives from the
+optimizer's bounded updates (with exact dyadic trajectories that make the bound tight), exact
+rational minimality of the exponents, torch's float8 and bf16 casts, numpy's fp32 arithmetic, and
+the output corruption the Transformers page warns about when fp32 scales are rounded up to UE8M0
+without re-quantizing."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from fp8_scaled_quantization_amd import workloads
+
+E4M3, E5M2 = 0, 1
+TENSOR, BLOCK, MX, MOSS, BLOCK_E8M0 = 0, 1, 2, 3, 4
+MAX = {E4M3: 448.0, E5M2: 57344.0}
+TORCH_FMT = {E4M3: torch.float8_e4m3fn, E5M2: torch.float8_e5m2}
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------------ history merge (Flax 5.3)
+def test_history_merge_worked_example(orc):
+    """Flax page section 5.3: one state used by in_qdq on 2.0 and on 3.0, merged by max, gives
+    scale 1.0 and history [3, 0, ..., 0]."""
+    with open(os.path.join(GOLDEN, "flax_fp32_max_grad_example.json")) as f:
+        g = json.load(f)
+    inp = g["inputs"]
+    branches = []
+    for v in (inp["x"], inp["y"]):
+        scale = np.array([inp["scale"]], np.float32)
+        hist = np.zeros(inp["history_len"], np.float32)
+        orc.delayed_step(np.array([[v]], np.float32), E4M3, scale, hist)
+        branches.append((scale, hist))
+    (s1, h1), (s2, h2) = branches
+    orc.history_merge(h1, s1, h2, s2[0])
+    want = g["max_merge"]
+    assert s1[0] == want["scale"]
+    assert list(h1[:1]) == want["history_head"] and np.all(h1[1:] == 0.0) and h1.size == 1024
+    # the page's contrast: summing the two updates gives 2.0 and [5, 0, ...]
+    assert s2[0] + 1.0 == g["sum_merge"]["scale"] and h2[0] + 2.0 == g["sum_merge"]["history_head"][0]
+
+
+def test_history_merge_is_a_semilattice(orc):
+    rng = np.random.default_rng(11)
+    a, b, c = (rng.standard_exponential(257).astype(np.float32) for _ in range(3))
+    sa, sb, sc = (np.array([v], np.float32) for v in rng.standard_exponential(3))
+
+    def merged(x, sx, y, sy):
+        h, s = x.copy(), sx.copy()
+        orc.history_merge(h, s, y, sy[0])
+        return h, s
+
+    ab, sab = merged(a, sa, b, sb)
+    ba, sba = merged(b, sb, a, sa)
+    assert np.array_equal(ab, ba) and sab[0] == sba[0]                            # commutative
+    aa, saa = merged(a, sa, a, sa)
+    assert np.array_equal(aa, a) and saa[0] == sa[0]                               # idempotent
+    l, sl = merged(*merged(a, sa, b, sb), c, sc)
+    r, sr = merged(a, sa, *merged(b, sb, c, sc))
+    assert np.array_equal(l, r) and sl[0] == sr[0]                                 # associative
+    assert np.array_equal(ab, np.maximum(a, b)) and sab[0] == max(sa[0], sb[0])    # the max
+    ninf = np.full(257, -np.inf, np.float32)
+    e, se = merged(a, sa, ninf, np.array([-np.inf], np.float32))
+    assert np.array_equal(e, a) and se[0] == sa[0]                                 # -inf is the unit
+    n = a.copy()
+    n[5] = np.nan
+    m, _ = merged(n, sa, b, sb)
+    assert np.isnan(m[5]) and np.array_equal(np.delete(m, 5), np.delete(np.maximum(a, b), 5))
+
+
+# ------------------------------------------------------------------ automatic scaling (MOSS 5)
+def _jit_scale(orc, w, fmt):
+    return orc.compute_scale(orc.amax(w), fmt, 1.0)
+
+
+def _trajectory(rng, w0, lrs, worst_case_index=None):
+    """Weights after each step with every element moved by at most that step's learning rate
+    (the MOSS page's bound on an Adam/AdamW update)."""
+    ws = [w0]
+    w = w0.astype(np.float64)
+    for lr in lrs:
+        step = rng.uniform(-1.0, 1.0, w.shape) * lr
+        if worst_case_index is not None:
+            step.flat[worst_case_index] = lr * np.sign(w.flat[worst_case_index])
+        w = w + step
+        ws.append(w.astype(np.float32))
+    return ws
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_auto_scale_is_an_upper_bound_and_rescales_to_jit(orc, fmt):
+    rng = np.random.default_rng(5 + fmt)
+    steps, interval = 1200, 500
+    lrs = (3e-4 * (1 + np.cos(np.arange(steps) / steps * np.pi)) / 2 + 1e-5).astype(np.float32)   # cosine schedule
+    ws = _trajectory(rng, (0.02 * rng.standard_normal((64, 96))).astype(np.float32), lrs, worst_case_index=77)
+    state = np.zeros(2, np.float32)
+    for t in range(steps):
+        rescale = t % interval == 0
+        s = orc.auto_scale_step(state, rescale, orc.amax(ws[t]) if rescale else 0.0, lrs[t], fmt)
+        jit = _jit_scale(orc, ws[t], fmt)
+        if rescale:
+            assert s == jit, t                      # the interval starts from a fresh max-reduction
+        # never below the just-in-time scale (no overflow), up to the fp32 rounding of the running
+        # learning-rate sum and of the weights themselves (a few ulps; one step's lr is ~2^-8
+        # of the weight max here, so a missed or extra step fails by far more)
+        assert s >= jit * (1.0 - 2.0 ** -21), (t, s, jit)
+
+
+def test_auto_scale_is_tight_on_the_worst_case_trajectory(orc):
+    """The largest weight grows by exactly the learning rate every step (dyadic values, so every
+    sum is exact in fp32): the predicted max equals the true max at every step, so the predicted
+    scale equals the just-in-time scale -- an off-by-one in the step count fails this."""
+    lr = np.float32(2.0 ** -10)
+    w = np.zeros((4, 8), np.float32)
+    w[1, 3] = 1.0
+    state = np.zeros(2, np.float32)
+    for t in range(600):
+        rescale = t % 500 == 0
+        s = orc.auto_scale_step(state, rescale, orc.amax(w) if rescale else 0.0, lr, E4M3)
+        assert s == _jit_scale(orc, w, E4M3), t
+        w[1, 3] += lr                              # the optimizer step after the forward pass
+
+
+def test_auto_scale_zero_weight_falls_back(orc):
+    state = np.zeros(2, np.float32)
+    assert orc.auto_scale_step(state, True, 0.0, 0.0, E4M3) == 1.0
+    assert orc.auto_scale_step(state, False, 0.0, 0.0, E4M3) == 1.0
+    assert state[0] == 0.0 and state[1] == 0.0
+
+
+# ------------------------------------------------------------------ UE8M0 block scales (HF 七)
+def _min_exponent(amax, fmt):
+    """Smallest integer e with MAX * 2^e >= amax, by exact rational arithmetic."""
+    a = Fraction(float(amax))
+    e = -127
+    while e < 127 and Fraction(MAX[fmt]) * Fraction(2) ** e < a:
+        e += 1
+    return e
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("br,bc", [(128, 128), (32, 32), (1, 32)])
+def test_block_e8m0_exponents_minimal_and_torch_cast(orc, fmt, br, bc):
+    xb = workloads.random_matrix(40 + br, 200, 264, 0.03)        # ragged in both directions
+    x = workloads.bf16_bits_to_f32(xb)
+    q, e8 = orc.quantize_block_e8m0(xb, fmt, br, bc)
+    R, C = x.shape
+    for bi in range(e8.shape[0]):
+        for bj in range(e8.shape[1]):
+            blk = x[bi * br:(bi + 1) * br, bj * bc:(bj + 1) * bc]
+            e = int(e8[bi, bj]) - 127
+            assert e == _min_exponent(np.abs(blk).max(), fmt)
+            v = torch.from_numpy(blk.copy()) * (2.0 ** -e)                # exact power-of-two scaling
+            assert float(v.abs().max()) <= MAX[fmt]                       # nothing clips
+            want = v.to(TORCH_FMT[fmt]).view(torch.uint8).numpy()
+            assert np.array_equal(q[bi * br:(bi + 1) * br, bj * bc:(bj + 1) * bc], want)
+
+
+def test_block_e8m0_one_by_32_is_mx(orc):
+    xb = workloads.random_matrix(3, 64, 256, 1.0)
+    q1, e1 = orc.quantize_block_e8m0(xb, E4M3, 1, 32)
+    q2, e2 = orc.quantize_mx(xb, E4M3)
+    assert np.array_equal(q1, q2) and np.array_equal(e1, e2)
+
+
+def test_scales_f32_to_e8m0_exact(orc):
+    e = np.arange(-127, 128)
+    s = np.ldexp(np.float32(1.0), e).astype(np.float32)
+    assert np.all(s == np.ldexp(1.0, e))                   # every 2^e, e in [-127, 127], is exact in fp32
+    b, bad = orc.scales_f32_to_e8m0(s)
+    assert bad == 0 and np.array_equal(b.astype(int), e + 127)
+    junk = np.array([3.0, 0.75, 0.0, -1.0, np.inf, np.nan, np.float32(2.0 ** -127) * 3, 1.0 + 2.0 ** -23], np.float32)
+    b, bad = orc.scales_f32_to_e8m0(junk)
+    assert bad == junk.size and np.all(b == 0xFF)
+
+
+def test_rounding_fp32_block_scales_up_without_requantizing_corrupts(orc):
+    """The Transformers page (section 七): rounding fp32 block scales up to UE8M0 while keeping the
+    FP8 bytes quantized with the fp32 scales silently changes the weights; re-quantizing with the
+    power-of-two scales keeps them within FP8 rounding error."""
+    W = workloads.random_matrix(9, 256, 384, 0.02)
+    w = workloads.bf16_bits_to_f32(W).astype(np.float64)
+    q, s = orc.quantize_block(W, E4M3, 128, 128)
+    good = orc.dequantize(BLOCK, q, E4M3, s, block=(128, 128))
+    s_up = np.ldexp(1.0, np.ceil(np.log2(s.astype(np.float64))).astype(np.int64)).astype(np.float32)   # ceil to a power of two
+    bad = orc.dequantize(BLOCK, q, E4M3, s_up, block=(128, 128))
+    ratio = np.abs(bad[good != 0] / good[good != 0])
+    assert np.all(ratio >= 1.0) and ratio.max() > 1.3                       # weights silently scaled up
+    rel_bad = np.linalg.norm(bad - w) / np.linalg.norm(w)
+    q8, e8 = orc.quantize_block_e8m0(W, E4M3, 128, 128)
+    req = orc.dequantize(BLOCK_E8M0, q8, E4M3, e8, block=(128, 128))
+    rel_req = np.linalg.norm(req - w) / np.linalg.norm(w)
+    assert rel_req < 0.04 < rel_bad                                         # E4M3 keeps ~2^-4 relative
+    nz = np.abs(w) > 2.0 ** -6 * np.ldexp(1.0, e8.astype(np.int64) - 127).repeat(128, 0).repeat(128, 1)
+    assert np.all(np.abs(req - w)[nz] <= 2.0 ** -4 * np.abs(w)[nz])       # normal range: half an ulp
+
+
+# ------------------------------------------------------------------ block dequantize (HF 五)
+def test_block_dequantize_fp32_scales_vs_numpy_and_torch(orc):
+    W = workloads.random_matrix(12, 300, 260, 0.05)
+    q, s = orc.quantize_block(W, E4M3, 128, 128)
+    dec = orc.decode_array(q, E4M3).astype(np.float32)
+    sfull = np.repeat(np.repeat(s, 128, 0), 128, 1)[:300, :260]
+    want32 = dec * sfull                                   # numpy fp32 multiply: IEEE round to nearest
+    got32 = orc.block_dequantize(BLOCK, q, E4M3, s, (128, 128), out_bf16=False)
+    assert np.array_equal(got32.view(np.uint32), want32.view(np.uint32))
+    gotbf = orc.block_dequantize(BLOCK, q, E4M3, s, (128, 128), out_bf16=True)
+    wantbf = torch.from_numpy(want32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(gotbf, wantbf)
+
+
+def test_block_dequantize_e8m0_is_exact(orc):
+    W = workloads.random_matrix(13, 256, 256, 0.05)
+    q, e8 = orc.quantize_block_e8m0(W, E4M3, 128, 128)
+    got32 = orc.block_dequantize(BLOCK_E8M0, q, E4M3, e8, (128, 128), out_bf16=False)
+    exact = orc.dequantize(BLOCK_E8M0, q, E4M3, e8, block=(128, 128))
+    assert np.array_equal(got32.astype(np.float64), exact)
+
+
+def test_static_activation_scale_is_a_constant_block_scale(orc):
+    """Static activations (one supplied scale for the whole tensor) dequantize exactly like 1x128
+    activation blocks that all carry that scale."""
+    xb = workloads.random_matrix(14, 64, 384, 1.0)
+    s = np.float32(0.0123)
+    q = orc.quantize_tensor(xb, E4M3, s)
+    a = orc.dequantize(TENSOR, q, E4M3, None, s)
+    b = orc.dequantize(BLOCK, q, E4M3, np.full((64, 3), s, np.float32), block=(1, 128))
+    assert np.array_equal(a, b)
