@@ -18,10 +18,10 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_NO_DEVICE = 0, -1, -2, -3, -4
 E4M3, E5M2 = 0, 1
 IN_F32, IN_BF16 = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
-TENSOR, BLOCK, MX, MOSS = 0, 1, 2, 3
+TENSOR, BLOCK, MX, MOSS, BLOCK_E8M0 = 0, 1, 2, 3, 4
 
 EXPORTS = ("fp8q_init", "fp8q_last_error", "fp8_amax", "fp8_quantize", "fp8_quantize_dual", "fp8_history_update",
-           "fp8_scaled_gemm")
+           "fp8_scaled_gemm", "fp8_history_merge", "fp8_auto_scale", "fp8_scale_to_e8m0", "fp8_block_dequantize")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libfp8q.so is not built (run __graft_entry__.build() or "
@@ -43,6 +43,14 @@ _L.fp8_history_update.restype = _I
 _L.fp8_history_update.argtypes = [_P, _I64, _P, _P, _I, _P]
 _L.fp8_scaled_gemm.restype = _I
 _L.fp8_scaled_gemm.argtypes = [_I, _P, _I, _P, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _I, _I64, _P]
+_L.fp8_history_merge.restype = _I
+_L.fp8_history_merge.argtypes = [_P, _P, _I64, _P, _P, _P]
+_L.fp8_auto_scale.restype = _I
+_L.fp8_auto_scale.argtypes = [_P, _I, _P, ctypes.c_float, _I, _P, _P]
+_L.fp8_scale_to_e8m0.restype = _I
+_L.fp8_scale_to_e8m0.argtypes = [_P, _I64, _P, _P, _P]
+_L.fp8_block_dequantize.restype = _I
+_L.fp8_block_dequantize.argtypes = [_I, _I, _P, _I64, _I64, _I64, _P, _I, _I, _P, _I, _I64, _P]
 
 
 class Fp8qError(RuntimeError):
@@ -128,10 +136,39 @@ def fp8_scaled_gemm(mode: int, A: torch.Tensor, afmt: int, Ascale, B: torch.Tens
                               _ld(C), _stream(stream)))
 
 
+def fp8_history_merge(hist_dst: torch.Tensor, hist_src: torch.Tensor, scale_dst: torch.Tensor, scale_src: torch.Tensor,
+                      stream=None) -> None:
+    if hist_dst.numel() != hist_src.numel():
+        raise ValueError("histories differ in length")
+    _check(_L.fp8_history_merge(_ptr(hist_dst), _ptr(hist_src), hist_dst.numel(), _ptr(scale_dst), _ptr(scale_src),
+                                _stream(stream)))
+
+
+def fp8_auto_scale(state: torch.Tensor, rescale: bool, amax_now, lr: float, fmt: int, scale_out: torch.Tensor,
+                   stream=None) -> None:
+    _check(_L.fp8_auto_scale(_ptr(state), int(bool(rescale)), _ptr(amax_now), float(lr), fmt, _ptr(scale_out),
+                             _stream(stream)))
+
+
+def fp8_scale_to_e8m0(s: torch.Tensor, e8m0: torch.Tensor, bad_count: torch.Tensor, stream=None) -> None:
+    if s.numel() != e8m0.numel() or e8m0.dtype != torch.uint8 or bad_count.dtype != torch.int32:
+        raise TypeError("e8m0 must be uint8 with s's size and bad_count int32")
+    _check(_L.fp8_scale_to_e8m0(_ptr(s), s.numel(), _ptr(e8m0), _ptr(bad_count), _stream(stream)))
+
+
+def fp8_block_dequantize(mode: int, fmt: int, q: torch.Tensor, scales: torch.Tensor, out: torch.Tensor,
+                         block=(128, 128), stream=None) -> None:
+    out_dtype = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
+    _check(_L.fp8_block_dequantize(mode, fmt, _ptr(q), q.shape[0], q.shape[1], _ld(q), _ptr(scales), int(block[0]),
+                                   int(block[1]), _ptr(out), out_dtype, _ld(out), _stream(stream)))
+
+
 # ------------------------------------------------------------------ allocating conveniences
 def scale_shape(mode: int, out_rows: int, out_cols: int, block=(1, 128)):
     if mode == BLOCK:
         return (-(-out_rows // block[0]), -(-out_cols // block[1])), torch.float32
+    if mode == BLOCK_E8M0:
+        return (-(-out_rows // block[0]), -(-out_cols // block[1])), torch.uint8
     if mode in (MX, MOSS):
         return (out_rows, -(-out_cols // 32)), torch.uint8
     return None, None
@@ -176,3 +213,22 @@ def scaled_gemm(mode: int, A, afmt, Ascale, B, bfmt, Bscale, Aglobal=None, Bglob
                     device=A.device)
     fp8_scaled_gemm(mode, A, afmt, Ascale, B, bfmt, Bscale, Aglobal, Bglobal, C, out_dtype, stream)
     return C
+
+
+def scale_to_e8m0(s: torch.Tensor, stream=None) -> torch.Tensor:
+    """Exact fp32 -> UE8M0 conversion; raises ValueError if any scale is not an exact power of two in
+    range (the conversion never rounds: rounding block scales without re-quantizing corrupts weights)."""
+    e = torch.empty(s.shape, dtype=torch.uint8, device=s.device)
+    bad = torch.zeros(1, dtype=torch.int32, device=s.device)
+    fp8_scale_to_e8m0(s.contiguous(), e, bad, stream)
+    n = int(bad.item())
+    if n:
+        raise ValueError("%d of %d scales are not exact powers of two in [2^-127, 2^127]" % (n, s.numel()))
+    return e
+
+
+def block_dequantize(mode: int, fmt: int, q: torch.Tensor, scales: torch.Tensor, block=(128, 128),
+                     out_dtype: int = OUT_BF16, stream=None) -> torch.Tensor:
+    out = torch.empty(q.shape, dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32, device=q.device)
+    fp8_block_dequantize(mode, fmt, q, scales, out, block, stream)
+    return out

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp8q.so")
-SOURCES = ["capi.hip", "amax_history.hip", "quantize.hip", "gemm.hip"]
+SOURCES = ["capi.hip", "amax_history.hip", "quantize.hip", "gemm.hip", "next.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

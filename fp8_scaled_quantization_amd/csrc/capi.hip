@@ -76,7 +76,7 @@ int fp8_quantize(int mode, int fmt, const void* x, int in_dtype, int64_t rows, i
                  int block_r, int block_c, int transpose_out, uint8_t* q, int64_t ldq, void* scales,
                  float* tensor_scale, int scale_is_input, float* amax_out, void* stream) {
     g_err[0] = 0;
-    if (mode < FP8Q_TENSOR || mode > FP8Q_MOSS) return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: unknown mode %d", mode);
+    if (mode < FP8Q_TENSOR || mode > FP8Q_BLOCK_E8M0) return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: unknown mode %d", mode);
     if (!valid_fmt(fmt)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: fmt %d is not FP8Q_E4M3/E5M2", fmt);
     if (!valid_in(in_dtype)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: in_dtype %d is not FP8Q_IN_F32/BF16", in_dtype);
     if (transpose_out != 0 && transpose_out != 1) return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: transpose_out must be 0 or 1");
@@ -87,7 +87,7 @@ int fp8_quantize(int mode, int fmt, const void* x, int in_dtype, int64_t rows, i
                              (long long)ldq, (long long)K);
     const bool empty = rows * cols == 0;
     if (!empty && (!x || !q)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: NULL x or q");
-    if (mode == FP8Q_BLOCK && (block_r <= 0 || block_c <= 0))
+    if ((mode == FP8Q_BLOCK || mode == FP8Q_BLOCK_E8M0) && (block_r <= 0 || block_c <= 0))
         return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: block size (%d, %d) must be two positive integers", block_r, block_c);
     if (mode != FP8Q_TENSOR && !scales && !empty) return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: NULL scales");
     const bool needs_amax = (mode == FP8Q_TENSOR || mode == FP8Q_MOSS) && !scale_is_input;
@@ -231,7 +231,7 @@ int fp8_scaled_gemm(int mode, const uint8_t* A, int afmt, const void* Ascale, co
                     const void* Bscale, const float* Aglobal, const float* Bglobal, int64_t M, int64_t N, int64_t K,
                     int64_t lda, int64_t ldb, void* C, int out_dtype, int64_t ldc, void* stream) {
     g_err[0] = 0;
-    if (mode < FP8Q_TENSOR || mode > FP8Q_MOSS) return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: unknown mode %d", mode);
+    if (mode < FP8Q_TENSOR || mode > FP8Q_BLOCK_E8M0) return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: unknown mode %d", mode);
     if (!valid_fmt(afmt) || !valid_fmt(bfmt)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: bad operand format");
     if (out_dtype != FP8Q_OUT_F32 && out_dtype != FP8Q_OUT_BF16)
         return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: out_dtype %d is not FP8Q_OUT_F32/BF16 (it is required)", out_dtype);
@@ -242,14 +242,19 @@ int fp8_scaled_gemm(int mode, const uint8_t* A, int afmt, const void* Ascale, co
     if (M * N * K > 0 && (!A || !B)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: NULL A or B");
     if ((mode == FP8Q_TENSOR || mode == FP8Q_MOSS) && (!Aglobal || !Bglobal))
         return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: Aglobal and Bglobal are required for TENSOR and MOSS");
-    if (mode != FP8Q_TENSOR && K > 0 && M * N > 0 && (!Ascale || !Bscale))
-        return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: Ascale and Bscale are required for BLOCK, MX and MOSS");
+    const bool blocked = mode == FP8Q_BLOCK || mode == FP8Q_BLOCK_E8M0;
+    const bool a_static = blocked && !Ascale && Aglobal;     // static per-tensor activation scale
+    if (mode != FP8Q_TENSOR && K > 0 && M * N > 0 && ((!Ascale && !a_static) || !Bscale))
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: Ascale (or, for BLOCK, a static Aglobal) and Bscale are "
+                    "required for BLOCK, BLOCK_E8M0, MX and MOSS");
     if (K > 0 && (K % 16 || lda % 16 || ldb % 16 || !aligned16(A) || !aligned16(B)))
         return fail(FP8Q_ERR_UNSUPPORTED, "fp8_scaled_gemm: needs K, lda, ldb multiples of 16 and 16-byte aligned A, B");
     int rc = check_device();
     if (rc) return rc;
     fp8q::GemmArgs g{};
     g.mode = mode;
+    g.a_static = a_static;
+    g.b_e8m0 = mode == FP8Q_BLOCK_E8M0;
     g.afmt = afmt;
     g.bfmt = bfmt;
     g.A = A;
@@ -268,6 +273,77 @@ int fp8_scaled_gemm(int mode, const uint8_t* A, int afmt, const void* Ascale, co
     g.ldc = ldc;
     fp8q::launch_gemm(g, static_cast<hipStream_t>(stream));
     return check_launch("fp8_scaled_gemm");
+}
+
+int fp8_history_merge(float* hist_dst, const float* hist_src, int64_t len, float* scale_dst, const float* scale_src,
+                      void* stream) {
+    g_err[0] = 0;
+    if (len < 0) return fail(FP8Q_ERR_INVALID_ARG, "fp8_history_merge: len=%lld < 0", (long long)len);
+    if (!scale_dst || !scale_src || (len > 0 && (!hist_dst || !hist_src)))
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_history_merge: NULL pointer");
+    int rc = check_device();
+    if (rc) return rc;
+    fp8q::launch_history_merge(hist_dst, hist_src, len, scale_dst, scale_src, static_cast<hipStream_t>(stream));
+    return check_launch("fp8_history_merge");
+}
+
+int fp8_auto_scale(float* state, int rescale, const float* amax_now, float lr, int fmt, float* scale_out, void* stream) {
+    g_err[0] = 0;
+    if (!valid_fmt(fmt)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_auto_scale: fmt %d is not FP8Q_E4M3/E5M2", fmt);
+    if (rescale != 0 && rescale != 1) return fail(FP8Q_ERR_INVALID_ARG, "fp8_auto_scale: rescale must be 0 or 1");
+    if (!state || !scale_out || (rescale && !amax_now)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_auto_scale: NULL pointer");
+    if (!(lr >= 0.0f) || lr == __builtin_huge_valf())
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_auto_scale: the learning rate must be finite and >= 0");
+    int rc = check_device();
+    if (rc) return rc;
+    fp8q::launch_auto_scale(state, rescale, amax_now, lr, fmt, scale_out, static_cast<hipStream_t>(stream));
+    return check_launch("fp8_auto_scale");
+}
+
+int fp8_scale_to_e8m0(const float* s, int64_t n, uint8_t* e8m0, int32_t* bad_count, void* stream) {
+    g_err[0] = 0;
+    if (n < 0) return fail(FP8Q_ERR_INVALID_ARG, "fp8_scale_to_e8m0: n=%lld < 0", (long long)n);
+    if (!bad_count || (n > 0 && (!s || !e8m0))) return fail(FP8Q_ERR_INVALID_ARG, "fp8_scale_to_e8m0: NULL pointer");
+    int rc = check_device();
+    if (rc) return rc;
+    fp8q::launch_scale_to_e8m0(s, n, e8m0, bad_count, static_cast<hipStream_t>(stream));
+    return check_launch("fp8_scale_to_e8m0");
+}
+
+int fp8_block_dequantize(int mode, int fmt, const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const void* scales,
+                         int block_r, int block_c, void* out, int out_dtype, int64_t ldo, void* stream) {
+    g_err[0] = 0;
+    if (mode != FP8Q_BLOCK && mode != FP8Q_BLOCK_E8M0)
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_block_dequantize: mode %d is not FP8Q_BLOCK/BLOCK_E8M0", mode);
+    if (!valid_fmt(fmt)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_block_dequantize: fmt %d is not FP8Q_E4M3/E5M2", fmt);
+    if (out_dtype != FP8Q_OUT_F32 && out_dtype != FP8Q_OUT_BF16)
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_block_dequantize: out_dtype %d is not FP8Q_OUT_F32/BF16", out_dtype);
+    if (block_r <= 0 || block_c <= 0)
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_block_dequantize: block size (%d, %d) must be two positive integers",
+                    block_r, block_c);
+    if (rows < 0 || cols < 0 || ldq < cols || ldo < cols)
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_block_dequantize: bad shape rows=%lld cols=%lld ldq=%lld ldo=%lld",
+                    (long long)rows, (long long)cols, (long long)ldq, (long long)ldo);
+    if (rows * cols > 0 && (!q || !scales || !out)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_block_dequantize: NULL pointer");
+    int rc = check_device();
+    if (rc) return rc;
+    fp8q::DequantArgs a{};
+    a.e8m0 = mode == FP8Q_BLOCK_E8M0;
+    a.fmt = fmt;
+    a.q = q;
+    a.rows = rows;
+    a.cols = cols;
+    a.ldq = ldq;
+    a.scales = scales;
+    a.block_r = block_r;
+    a.block_c = block_c;
+    a.out = out;
+    a.out_bf16 = out_dtype == FP8Q_OUT_BF16;
+    a.ldo = ldo;
+    const int64_t esz = a.out_bf16 ? 2 : 4;
+    a.vec = cols % 16 == 0 && block_c % 16 == 0 && ldq % 16 == 0 && (ldo * esz) % 16 == 0 && aligned16(q) && aligned16(out);
+    fp8q::launch_block_dequantize(a, static_cast<hipStream_t>(stream));
+    return check_launch("fp8_block_dequantize");
 }
 
 }  // extern "C"

@@ -6,7 +6,8 @@
 //           section 2.2: FP32-accumulated dot, dequantize by a_scale * b_scale);
 //   BLOCK   each 128-wide K block's FP32 partial is multiplied by fl(sx[m][kb] * sw[n/128][kb]) and
 //           accumulated in the main loop (page "Transformers 中的细粒度 FP8 量化配置 ...", section 一:
-//           1x128 activation groups aligned with 128x128 weight blocks);
+//           1x128 activation groups aligned with 128x128 weight blocks); sw may be an E8M0 power
+//           of two (section 七) and sx one static per-tensor activation scale (section 四);
 //   MX      the E8M0 scales of each 32-wide K group go into the block-scaled MFMA
 //           (v_mfma_scale_f32_16x16x128_f8f6f4), so the main loop is matrix-core only (page "MOSS:
 //           高效、精确的 FP8 LLM 训练 ...", sections 1 and 4);
@@ -116,7 +117,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         } else if (MODE == kModeBlock) {
             if (t < 128) {
                 const int64_t grow = m0 + t;
-                rsa = grow < M ? static_cast<const uint32_t*>(g.Ascale)[grow * nkb + kt] : 0u;
+                if (g.a_static) rsa = __float_as_uint(*g.Aglobal);
+                else rsa = grow < M ? static_cast<const uint32_t*>(g.Ascale)[grow * nkb + kt] : 0u;
             }
         }
     };
@@ -175,7 +177,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         float rowscale[4][4];
         if (MODE == kModeBlock) {
             const int64_t nb = n0 / 128;
-            const float sw = static_cast<const float*>(g.Bscale)[nb * nkb + kt];
+            const float sw = g.b_e8m0 ? __builtin_amdgcn_ldexpf(1.0f, (int)static_cast<const uint8_t*>(g.Bscale)[nb * nkb + kt] - 127)
+                                      : static_cast<const float*>(g.Bscale)[nb * nkb + kt];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -311,7 +314,8 @@ int launch_gemm(const GemmArgs& g, hipStream_t st) {
     if (g.M == 0 || g.N == 0) return 0;
     switch (g.mode) {
         case kModeTensor: launch_fmt<kModeTensor>(g, st); break;
-        case kModeBlock: launch_fmt<kModeBlock>(g, st); break;
+        case kModeBlock:
+        case kModeBlockE8: launch_fmt<kModeBlock>(g, st); break;   // b_e8m0 / a_static select the scale kinds
         case kModeMX: launch_fmt<kModeMX>(g, st); break;
         default: launch_fmt<kModeMoss>(g, st); break;
     }

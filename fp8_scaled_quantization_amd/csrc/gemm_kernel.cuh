@@ -5,6 +5,8 @@
 //           section 2.2);
 //   BLOCK   each 128-wide K block's FP32 partial is scaled by fl(sx[m][kb] * sw[n/128][kb]) and
 //           accumulated in the main loop (page "Transformers 中的细粒度 FP8 量化配置 ...", section 一);
+//           sw may be an E8M0 power of two (section 七) and sx one static per-tensor activation
+//           scale (section 四);
 //   MX/MOSS E8M0 scales per 32-wide K group applied by v_mfma_scale_f32_16x16x128_f8f6f4; MOSS adds
 //           fl(S_A*S_B) in the epilogue (page "MOSS:高效、精确的 FP8 LLM 训练 ...", sections 1, 4).
 //
@@ -83,6 +85,23 @@ __device__ __forceinline__ float load_uniform_f32(const float* p) {
     const uint64_t u = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a) |
                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) << 32);
     return *(cptr)u;
+}
+
+// Read-only load of the byte at p (wave-uniform address) through the scalar cache: the aligned
+// 4-byte word holding it is fetched (an aligned word never crosses a page, so it is readable when
+// the byte is) and the byte extracted.
+__device__ __forceinline__ uint32_t load_uniform_u8(const uint8_t* p) {
+    typedef __attribute__((address_space(4))) const uint32_t* cptr;
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint64_t u = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a) |
+                       ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) << 32);
+    return (*(cptr)(u & ~(uint64_t)3) >> (8 * (uint32_t)(u & 3))) & 0xFFu;
+}
+
+// 128x128 weight-block scale of (n-block, k-block) index bi: fp32, or an E8M0 byte (2^(b - 127))
+__device__ __forceinline__ float weight_block_scale(const GemmArgs& g, int64_t bi) {
+    if (g.b_e8m0) return __builtin_amdgcn_ldexpf(1.0f, (int)load_uniform_u8(static_cast<const uint8_t*>(g.Bscale) + bi) - 127);
+    return load_uniform_f32(static_cast<const float*>(g.Bscale) + bi);
 }
 
 // wait until at most N vector-memory operations of this wave are outstanding
@@ -184,10 +203,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmArgs g
     const uint8_t* sca_base = static_cast<const uint8_t*>(g.Ascale);
     const uint8_t* scb_base = static_cast<const uint8_t*>(g.Bscale);
     uint32_t sca_bytes = 0, scb_bytes = 0;
-    if (SCALED || BLOCKED) {
+    if (SCALED || (BLOCKED && !g.a_static)) {
         sca_base += m0 * sc_row;
         sca_bytes = (uint32_t)(max((int64_t)0, M - m0) * sc_row);
     }
+    // static activation scale (BLOCK with one per-tensor activation scale): the per-row scale
+    // quads read as zeros (empty buffer range) and the tensor scale stands in for them
+    const float a_static = (BLOCKED && g.a_static) ? load_uniform_f32(g.Aglobal) : 0.0f;
     if (SCALED) {
         scb_base += n0 * sc_row;
         scb_bytes = (uint32_t)(max((int64_t)0, N - n0) * sc_row);
@@ -269,7 +291,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmArgs g
             if (SCALED) scb[j] = (int)((sqB[(wn * WTN + j * 16 + r16) * 4 + qs] >> (8 * g4)) & 0xFFu);
         }
         float sw = 1.0f;
-        if (BLOCKED) sw = load_uniform_f32(static_cast<const float*>(g.Bscale) + (n0 / 128) * nkb + kt);
+        if (BLOCKED) sw = weight_block_scale(g, (n0 / 128) * nkb + kt);
 
         // A fragments: the next subtile's reads are issued before this subtile's MFMAs
         v8i fa_next;
@@ -294,7 +316,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmArgs g
                 float rs[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    rs[e] = __uint_as_float(sqA[(wm * WTM + i * 16 + 4 * g4 + e) * 4 + qs]) * sw;
+                    rs[e] = (g.a_static ? a_static : __uint_as_float(sqA[(wm * WTM + i * 16 + 4 * g4 + e) * 4 + qs])) * sw;
                 v4f p[TN];
 #pragma unroll
                 for (int j = 0; j < TN; ++j)

@@ -7,7 +7,7 @@
 namespace fp8q {
 
 constexpr int64_t kMaxReduceBlocks = 256;    // cap on workgroups that each end with one same-address atomic
-constexpr int kModeTensor = 0, kModeBlock = 1, kModeMX = 2, kModeMoss = 3;
+constexpr int kModeTensor = 0, kModeBlock = 1, kModeMX = 2, kModeMoss = 3, kModeBlockE8 = 4;
 
 int launch_amax(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ld, float* amax_out,
                 hipStream_t st);
@@ -45,6 +45,9 @@ int launch_cast(const CastArgs& a, hipStream_t st);
 
 struct GemmArgs {
     int mode, afmt, bfmt;
+    // BLOCK / BLOCK_E8M0 only: a_static = the activation operand has one per-tensor scale, *Aglobal
+    // (Ascale unused); b_e8m0 = the 128x128 weight-block scales are E8M0 bytes (else fp32)
+    bool a_static, b_e8m0;
     const uint8_t* A;
     const uint8_t* B;
     const void* Ascale;
@@ -57,5 +60,25 @@ struct GemmArgs {
     int64_t ldc;
 };
 int launch_gemm(const GemmArgs& g, hipStream_t st);
+
+// Small state kernels and block dequantization (next.hip).
+int launch_history_merge(float* hist_dst, const float* hist_src, int64_t len, float* scale_dst,
+                         const float* scale_src, hipStream_t st);
+int launch_auto_scale(float* state, int rescale, const float* amax_now, float lr, int fmt, float* scale_out,
+                      hipStream_t st);
+int launch_scale_to_e8m0(const float* s, int64_t n, uint8_t* e8m0, int32_t* bad_count, hipStream_t st);
+struct DequantArgs {
+    bool e8m0;                 // block scales are E8M0 bytes (else fp32)
+    int fmt;
+    const uint8_t* q;
+    int64_t rows, cols, ldq;
+    const void* scales;
+    int block_r, block_c;
+    void* out;
+    bool out_bf16;
+    int64_t ldo;
+    bool vec;                  // 16-byte aligned rows (q, out) and cols % 16 == 0, block_c % 16 == 0
+};
+int launch_block_dequantize(const DequantArgs& a, hipStream_t st);
 
 }  // namespace fp8q

@@ -8,7 +8,9 @@
 //   MX      a power of two per 32 consecutive K values, chosen so that nothing clips (page "MOSS:
 //           高效、精确的 FP8 LLM 训练 ...", section 1); the element is x * 2^-e, exact scaling;
 //   MOSS    fp32 global S times a per-32 power-of-two local factor in (0, 1] (same page, section 4);
-//           the element is fl(x / S) * 2^-e_i.
+//           the element is fl(x / S) * 2^-e_i;
+//   BLOCK_E8M0  one power-of-two (UE8M0) scale per block, chosen like MX so that nothing clips
+//           (page "Transformers 中的细粒度 FP8 量化配置 ...", section 七); element x * 2^-e.
 //
 // Work layout.  A "lane chunk" is 32 consecutive values along the output's K axis, owned by one
 // lane: an MX/MOSS group is exactly one lane (no cross-lane reduction) and a 1x128 group is four
@@ -370,7 +372,7 @@ __global__ __launch_bounds__(kTileThreads) void cast_transposed_kernel(CastArgs 
 // ------------------------------------------------------------------ 128x128 weight blocks
 // One workgroup per 128x128 block (non-transposed, rows % 128 == 0, cols % 128 == 0): thread t
 // holds row t/2, columns (t%2)*64 .. +64 in registers; block amax via LDS; one pass over HBM.
-template <int FMT, bool BF16>
+template <int FMT, bool BF16, bool E8>
 __global__ __launch_bounds__(256) void cast_block128_kernel(CastArgs a) {
     const int64_t br = blockIdx.y, bc = blockIdx.x;
     const int t = threadIdx.x;
@@ -386,15 +388,23 @@ __global__ __launch_bounds__(256) void cast_block128_kernel(CastArgs a) {
     if ((t & 63) == 0) red[t >> 6] = m;
     __syncthreads();
     const uint32_t bm = max(max(red[0], red[1]), max(red[2], red[3]));
-    const float s = scale_from_amax<FMT>(__uint_as_float(bm), 1.0f);
-    const float y = recip_rn(s);
     uint32_t out[16];
-    cast_div<FMT, false, 32>(v, s, y, 0, divisor_ok(s) && dividends_ok(m0, chunk_min_m1<32>(v)), out);
-    cast_div<FMT, false, 32>(v + 32, s, y, 0, divisor_ok(s) && dividends_ok(m1, chunk_min_m1<32>(v + 32)), out + 8);
+    if constexpr (E8) {
+        // power-of-two block scale: the MX exponent rule over the whole block, exact scaling
+        const int e = mx_exponent<FMT>(__uint_as_float(bm));
+        cast_mx<FMT, 32>(v, -e, m0 > 0x7F800000u, out);
+        cast_mx<FMT, 32>(v + 32, -e, m1 > 0x7F800000u, out + 8);
+        if (t == 0) reinterpret_cast<uint8_t*>(a.scales)[br * (a.cols / 128) + bc] = (uint8_t)(e + 127);
+    } else {
+        const float s = scale_from_amax<FMT>(__uint_as_float(bm), 1.0f);
+        const float y = recip_rn(s);
+        cast_div<FMT, false, 32>(v, s, y, 0, divisor_ok(s) && dividends_ok(m0, chunk_min_m1<32>(v)), out);
+        cast_div<FMT, false, 32>(v + 32, s, y, 0, divisor_ok(s) && dividends_ok(m1, chunk_min_m1<32>(v + 32)), out + 8);
+        if (t == 0) reinterpret_cast<float*>(a.scales)[br * (a.cols / 128) + bc] = s;
+    }
     uint8_t* dst = a.q + r * a.ldq + c;
     store32(dst, out);
     store32(dst + 32, out + 8);
-    if (t == 0) reinterpret_cast<float*>(a.scales)[br * (a.cols / 128) + bc] = s;
 }
 
 // ------------------------------------------------------------------ generic exact fallback
@@ -432,7 +442,7 @@ __global__ __launch_bounds__(256) void cast_generic_kernel(CastArgs a, int br, i
     } else if (MODE == kModeBlock) {
         s = scale_from_amax<FMT>(bamax, 1.0f);
         if (threadIdx.x == 0) reinterpret_cast<float*>(a.scales)[bi * nbc + bj] = s;
-    } else if (MODE == kModeMX) {
+    } else if (MODE == kModeMX || MODE == kModeBlockE8) {
         int e = mx_exponent<FMT>(bamax);
         shift = -e;
         if (threadIdx.x == 0) reinterpret_cast<uint8_t*>(a.scales)[bi * nbc + bj] = (uint8_t)(e + 127);
@@ -445,7 +455,7 @@ __global__ __launch_bounds__(256) void cast_generic_kernel(CastArgs a, int br, i
     }
     for (int64_t i = threadIdx.x; i < n; i += 256) {
         float x = load(i);
-        float v = (MODE == kModeMX) ? x : x / s;
+        float v = (MODE == kModeMX || MODE == kModeBlockE8) ? x : x / s;
         v = __builtin_amdgcn_ldexpf(v, shift);
         a.q[(rb + i / kn) * a.ldq + kb + i % kn] = (uint8_t)code_slow<FMT>(v);
     }
@@ -461,19 +471,26 @@ static void dispatch_shape(const CastArgs& a, hipStream_t st) {
     if (!a.vec_out) {
         int br = 1, bc = 32;
         if (MODE == kModeTensor) { br = 1; bc = 256; }
-        if (MODE == kModeBlock) { br = a.block_r; bc = a.block_c; }
+        if (MODE == kModeBlock || MODE == kModeBlockE8) { br = a.block_r; bc = a.block_c; }
         dim3 grid((unsigned)((K + bc - 1) / bc), (unsigned)((R + br - 1) / br));
         hipLaunchKernelGGL((cast_generic_kernel<FMT, MODE, BF16, FUSED, DERIVE>), grid, dim3(256), 0, st, a, br, bc);
         return;
     }
-    const bool block128 = MODE == kModeBlock && a.block_r == 128 && a.block_c == 128;
+    const bool block128 = (MODE == kModeBlock || MODE == kModeBlockE8) && a.block_r == 128 && a.block_c == 128;
+    if (!a.transpose && block128 && !FUSED && a.rows % 128 == 0 && a.cols % 128 == 0) {
+        hipLaunchKernelGGL((cast_block128_kernel<FMT, BF16, MODE == kModeBlockE8>),
+                           dim3((unsigned)(a.cols / 128), (unsigned)(a.rows / 128)), dim3(256), 0, st, a);
+        return;
+    }
+    if constexpr (MODE == kModeBlockE8) {
+        // other UE8M0 block shapes and transposed outputs: the exact per-block kernel
+        dim3 grid((unsigned)((K + a.block_c - 1) / a.block_c), (unsigned)((R + a.block_r - 1) / a.block_r));
+        hipLaunchKernelGGL((cast_generic_kernel<FMT, MODE, BF16, FUSED, DERIVE>), grid, dim3(256), 0, st, a, a.block_r,
+                           a.block_c);
+        return;
+    } else {
     const bool row_group_ok = MODE != kModeBlock || (a.block_r == 1 && a.block_c == 128);
     if (!a.transpose) {
-        if (block128 && !FUSED && a.rows % 128 == 0 && a.cols % 128 == 0) {
-            hipLaunchKernelGGL((cast_block128_kernel<FMT, BF16>), dim3((unsigned)(a.cols / 128), (unsigned)(a.rows / 128)),
-                               dim3(256), 0, st, a);
-            return;
-        }
         const int64_t kmod = MODE == kModeBlock ? 128 : 32;
         if (row_group_ok && a.cols % kmod == 0) {
             const int64_t total = a.rows * (a.cols / 32);
@@ -507,6 +524,7 @@ static void dispatch_shape(const CastArgs& a, hipStream_t st) {
     if (MODE == kModeBlock) { br = a.block_r; bc = a.block_c; }
     dim3 grid((unsigned)((K + bc - 1) / bc), (unsigned)((R + br - 1) / br));
     hipLaunchKernelGGL((cast_generic_kernel<FMT, MODE, BF16, FUSED, DERIVE>), grid, dim3(256), 0, st, a, br, bc);
+    }
 }
 
 template <int FMT, int MODE, bool BF16>
@@ -534,6 +552,7 @@ static void dispatch_mode(const CastArgs& a, hipStream_t st) {
         case kModeTensor: dispatch_in<FMT, kModeTensor>(a, st); break;
         case kModeBlock: dispatch_in<FMT, kModeBlock>(a, st); break;
         case kModeMX: dispatch_in<FMT, kModeMX>(a, st); break;
+        case kModeBlockE8: dispatch_in<FMT, kModeBlockE8>(a, st); break;
         default: dispatch_in<FMT, kModeMoss>(a, st); break;
     }
 }

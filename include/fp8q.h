@@ -9,17 +9,22 @@
  *  [FLAX] "Flax FP8 量化实战指南：从 fp8_ops 低层 API 到 Fp8DotGeneral / Fp8Einsum 的完整实现解析":
  *         section 1 (Q/DQ: scale = amax/MAX, x_fp8 = clip(x/scale), x ~= x_fp8 * scale),
  *         section 2.2 (current scaling; quantize = divide, clip to +-MAX, cast; FP32-accumulated
- *         dot; dequantize by a_scale * b_scale), section 2.3 (delayed scaling with an amax history).
+ *         dot; dequantize by a_scale * b_scale), section 2.3 (delayed scaling with an amax history),
+ *         section 5.3 (a state used by several branches merges their updates by max).
  *  [NANO] "Nanochat的FP8训练模块", section "实现" (E4M3/E5M2 and their maxima; the three GEMMs of a
  *         linear layer's forward and backward; output dtype always given explicitly; operand-layout
  *         bookkeeping is where transposes silently go wrong).
  *  [HF]   "Transformers 中的细粒度 FP8 量化配置、DeepGEMM 加速路径与 UE8M0 缩放格式完全指南":
  *         section 一 (128x128 weight blocks, 1x128 per-token activation groups, weight_scale_inv
- *         of shape (ceil(out/128), ceil(in/128))), section 四 (block size is two positive ints).
+ *         of shape (ceil(out/128), ceil(in/128))), section 四 (block size is two positive ints;
+ *         the static activation scheme with one supplied per-tensor activation scale), section 五
+ *         (dequantize: block scales folded back into the weights), section 七 (UE8M0 block scales,
+ *         exact conversion of power-of-two scales kept in fp32 containers).
  *  [MOSS] "MOSS:高效、精确的 FP8 LLM 训练,采用微尺度和自动尺度变换": section 1 (MXFP8: one
  *         power-of-two scale per 32 consecutive values), section 4 (two-level scaling: FP32 global
  *         factor = max of the per-32 factors, E8M0 local factor per 32 values, FP32 factors applied
- *         once in the GEMM epilogue).
+ *         once in the GEMM epilogue), section 5 (automatic weight scaling: the scale predicted from
+ *         the last measured weight max plus the learning rates since, re-measured every interval).
  *
  * Conventions for every entry point:
  *  - All data pointers are DEVICE pointers owned by the caller.  The library never allocates or
@@ -59,7 +64,8 @@ typedef enum {
     FP8Q_TENSOR = 0,   /* one fp32 scale for the tensor (current, delayed or static) */
     FP8Q_BLOCK = 1,    /* one fp32 scale per (block_r x block_c) block */
     FP8Q_MX = 2,       /* one E8M0 scale per 32 consecutive values along K */
-    FP8Q_MOSS = 3      /* fp32 global factor S times one E8M0 local factor per 32 values along K */
+    FP8Q_MOSS = 3,     /* fp32 global factor S times one E8M0 local factor per 32 values along K */
+    FP8Q_BLOCK_E8M0 = 4 /* one power-of-two (UE8M0 byte) scale per (block_r x block_c) block */
 } fp8q_mode;
 
 /* Checks that the current device is gfx950.  Called implicitly by every entry point; returns
@@ -114,6 +120,10 @@ int fp8_amax(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld
  *   receives amax_tensor, and S is written to *tensor_scale.  scale_is_input = 1: *tensor_scale
  *   holds S (from an earlier call on the same source tensor, e.g. the other copy of a
  *   forward/backward pair) and is not modified.
+ * mode FP8Q_BLOCK_E8M0 ([HF] section 七): per (block_r x block_c) block of the OUTPUT, e = smallest
+ *   integer in [-127, 127] with MAX * 2^e >= amax_block (127 if none), E8M0 byte e + 127 written to
+ *   `scales` as u8[ceil(R/block_r)][ceil(K/block_c)]; element = RNE8(clip(fl(x * 2^-e))) (exact
+ *   scaling: nothing clips unless the block holds Inf).  (128,128) is the UE8M0 weight scheme.
  *
  * Limits (FP8Q_ERR_UNSUPPORTED otherwise): cols % 8 == 0, ld % 8 == 0 and a 16-byte aligned x.
  * Any ldq >= K works (ldq % 16 == 0 with a 16-byte aligned q selects the vectorized kernels).
@@ -179,6 +189,12 @@ int fp8_history_update(float* history, int64_t len, const float* amax_new,
  *                scales are applied by the matrix-core instruction ([MOSS] section 1).
  *   FP8Q_MOSS:   as MX, plus Aglobal = &S_A, Bglobal = &S_B applied once in the epilogue as
  *                fl(S_A * S_B) ([MOSS] section 4).
+ *   FP8Q_BLOCK_E8M0: as FP8Q_BLOCK with Bscale u8 E8M0[ceil(N/128)][ceil(K/128)] (UE8M0 weight
+ *                blocks, [HF] section 七): sb = 2^(byte - 127).
+ *   Static activations ([HF] section 四, activation_scheme "static"): with FP8Q_BLOCK or
+ *                FP8Q_BLOCK_E8M0, Ascale = NULL and Aglobal = &s_a give every 1x128 activation
+ *                block the one per-tensor scale s_a (A quantized by fp8_quantize(FP8Q_TENSOR,
+ *                scale_is_input = 1)); the K-block factor is then fl(s_a * sb[n/128][kb]).
  * Accumulation: FP8Q_TENSOR, FP8Q_MX and FP8Q_MOSS keep the whole K sum in the FP8 matrix
  * instruction's FP32 accumulator; FP8Q_BLOCK reduces each 128-wide K chunk from zero and adds its
  * scaled FP32 partial into an FP32 accumulator.
@@ -190,6 +206,63 @@ int fp8_scaled_gemm(int mode, const uint8_t* A, int afmt, const void* Ascale,
                     const float* Aglobal, const float* Bglobal,
                     int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
                     void* C, int out_dtype, int64_t ldc, void* stream);
+
+/*
+ * fp8_history_merge -- combine the updates of one delayed-scaling state that was used by two
+ * branches ([FLAX] section 5.3: the Flax meta dtype adds by max, with -inf as its zero):
+ *     hist_dst[i] <- max(hist_dst[i], hist_src[i]),  *scale_dst <- max(*scale_dst, *scale_src)
+ * (a NaN on either side gives NaN).  hist_dst, hist_src: device fp32[len], len >= 0; scale_dst,
+ * scale_src: device fp32[1].  Merging each branch's state into one accumulator in turn gives the
+ * same result in any order.
+ */
+int fp8_history_merge(float* hist_dst, const float* hist_src, int64_t len,
+                      float* scale_dst, const float* scale_src, void* stream);
+
+/*
+ * fp8_auto_scale -- one step of automatic weight scaling ([MOSS] section 5): the weight max grows
+ * by at most the learning rate per optimizer step, so instead of a max-reduction of the weight the
+ * scale is predicted.
+ *   state: device fp32[2] owned by the caller, zero-initialised: state[0] = the weight max measured
+ *          at the current interval's start, state[1] = the learning rates summed since.
+ *   rescale = 1 on an interval's first step (every 500 steps on the page): state[0] <- *amax_now
+ *          (the caller's fp8_amax of the current weight), state[1] <- 0.  rescale = 0: amax_now is
+ *          not read (it may be NULL).
+ *   Then *scale_out <- fl(fl(state[0] + state[1]) / MAX) (1.0 when that max is 0 or non-finite),
+ *   and state[1] <- fl(state[1] + lr), lr being the learning rate of the optimizer step that
+ *   follows this forward pass.
+ * The scale is then used as the MOSS global factor (fp8_quantize(FP8Q_MOSS, scale_is_input = 1)) or
+ * as a per-tensor scale (FP8Q_TENSOR).  With fp32 arithmetic the prediction is an upper bound of
+ * the weight max up to the rounding of the running sum (a few ulps).
+ */
+int fp8_auto_scale(float* state, int rescale, const float* amax_now, float lr, int fmt,
+                   float* scale_out, void* stream);
+
+/*
+ * fp8_scale_to_e8m0 -- exact conversion of power-of-two scales stored as fp32 into UE8M0 bytes
+ * ([HF] section 七: checkpoints that keep UE8M0-style scales in fp32 containers are converted
+ * exactly on load).  s: device fp32[n]; e8m0: device u8[n] gets e + 127 for s = 2^e, e in
+ * [-127, 127].  Every other value (not a power of two, zero, negative, non-finite, out of range)
+ * has no exact UE8M0 form: it gets 0xFF and is counted into *bad_count (device int32, overwritten).
+ * A caller that requires exactness checks *bad_count == 0 (the Python binding raises ValueError).
+ * Scales are never rounded up here: rounding fp32 block scales up to UE8M0 without re-quantizing
+ * the weights silently changes them ([HF] section 七); use fp8_quantize(FP8Q_BLOCK_E8M0) instead.
+ */
+int fp8_scale_to_e8m0(const float* s, int64_t n, uint8_t* e8m0, int32_t* bad_count, void* stream);
+
+/*
+ * fp8_block_dequantize -- fold block scales back into an FP8 weight ([HF] section 五):
+ *     out[r][c] = fl(decode(q[r][c]) * s[r / block_r][c / block_c])     (one fp32 rounding)
+ * stored as fp32 or rounded to bf16 (round to nearest even; NaN stays NaN).
+ *   mode FP8Q_BLOCK: scales fp32[ceil(rows/block_r)][ceil(cols/block_c)]; FP8Q_BLOCK_E8M0: the same
+ *   shape of E8M0 bytes (s = 2^(byte - 127), so the product is exact).
+ *   q: rows x cols FP8 bytes (fmt), leading dimension ldq bytes; out: rows x cols, leading
+ *   dimension ldo elements, out_dtype FP8Q_OUT_F32 or FP8Q_OUT_BF16.
+ * cols % 16 == 0, block_c % 16 == 0 and 16-byte aligned rows select the vectorized kernel; any
+ * other shape is served element by element.
+ */
+int fp8_block_dequantize(int mode, int fmt, const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq,
+                         const void* scales, int block_r, int block_c,
+                         void* out, int out_dtype, int64_t ldo, void* stream);
 
 #ifdef __cplusplus
 }

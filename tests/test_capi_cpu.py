@@ -62,3 +62,26 @@ def test_invalid_arguments(L):
     assert g(0, dummy, 0, None, dummy, 0, None, None, None, 16, 16, 32, 32, 32, dummy, 0, 16, None) == L.ERR_INVALID_ARG
     assert g(2, dummy, 0, None, dummy, 0, None, None, None, 16, 16, 32, 32, 32, dummy, 0, 16, None) == L.ERR_INVALID_ARG
     assert g(0, dummy, 0, None, dummy, 0, None, dummy, dummy, 16, 16, 24, 32, 32, dummy, 0, 16, None) == L.ERR_UNSUPPORTED
+    # BLOCK_E8M0 is a quantize and GEMM mode, not a dual mode; static activations need Aglobal
+    assert lib.fp8_quantize(4, 0, dummy, 1, 4, 8, 8, 128, 0, 0, dummy, 16, dummy, None, 0, None, None) == L.ERR_INVALID_ARG
+    assert d(4, 0, dummy, 1, 32, 32, 32, dummy, 32, dummy, dummy, 32, dummy, dummy, 1, None, None) == L.ERR_INVALID_ARG
+    assert g(4, dummy, 0, None, dummy, 0, dummy, None, None, 16, 16, 128, 128, 128, dummy, 0, 16, None) == L.ERR_INVALID_ARG
+    assert g(5, dummy, 0, dummy, dummy, 0, dummy, None, None, 16, 16, 128, 128, 128, dummy, 0, 16, None) == L.ERR_INVALID_ARG
+
+
+def test_next_entry_points_reject_bad_arguments(L):
+    lib = L.lib()
+    dummy = ctypes.c_void_p(16)
+    assert lib.fp8_history_merge(dummy, dummy, -1, dummy, dummy, None) == L.ERR_INVALID_ARG
+    assert lib.fp8_history_merge(None, dummy, 8, dummy, dummy, None) == L.ERR_INVALID_ARG
+    assert lib.fp8_auto_scale(dummy, 1, None, ctypes.c_float(1e-3), 0, dummy, None) == L.ERR_INVALID_ARG
+    assert lib.fp8_auto_scale(dummy, 0, None, ctypes.c_float(-1.0), 0, dummy, None) == L.ERR_INVALID_ARG
+    assert "learning rate" in _err(L)
+    assert lib.fp8_auto_scale(dummy, 2, dummy, ctypes.c_float(1e-3), 0, dummy, None) == L.ERR_INVALID_ARG
+    assert lib.fp8_auto_scale(dummy, 0, None, ctypes.c_float(1e-3), 3, dummy, None) == L.ERR_INVALID_ARG
+    assert lib.fp8_scale_to_e8m0(dummy, 4, dummy, None, None) == L.ERR_INVALID_ARG
+    bd = lib.fp8_block_dequantize
+    assert bd(2, 0, dummy, 128, 128, 128, dummy, 128, 128, dummy, 1, 128, None) == L.ERR_INVALID_ARG
+    assert bd(1, 0, dummy, 128, 128, 128, dummy, 0, 128, dummy, 1, 128, None) == L.ERR_INVALID_ARG
+    assert bd(1, 0, dummy, 128, 128, 128, dummy, 128, 128, dummy, 5, 128, None) == L.ERR_INVALID_ARG
+    assert bd(4, 0, dummy, 128, 128, 64, dummy, 128, 128, dummy, 1, 128, None) == L.ERR_INVALID_ARG
