@@ -9,6 +9,10 @@ One step runs every scaling scheme's full path on its workload, with all inputs 
   MOSS fwd+bwd         X 16384x4096, W 4096x4096 (E4M3), dY 16384x4096 (E5M2): amax, then one
                        dual-axis cast per tensor (both quantized copies in one pass),
                        Y = X W^T, dX = dY W, dW = dY^T X
+After the timed steps, the next-step paths are timed on the same inputs (reported under
+"next_rows", not part of the headline): automatic weight scaling against a just-in-time max
+reduction of W, the delayed-scaling history merge, UE8M0 128x128 weight quantization and block
+dequantization, and the block GEMM with UE8M0 weight scales and with a static activation scale.
 The headline value is the step's total GEMM flops (2 M N K per GEMM) divided by the step time,
 i.e. scaled-GEMM TFLOP/s including every quantization the path performs.
 
@@ -47,8 +51,9 @@ def parse():
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                             "gemm_moss_16384x4096x4096_hbm_traffic.md")
-GEMM_SOURCES = ("fp8_scaled_quantization_amd/csrc/gemm_kernel.cuh", "fp8_scaled_quantization_amd/csrc/gemm.hip",
-                "fp8_scaled_quantization_amd/csrc/kernels.h", "fp8_scaled_quantization_amd/csrc/common.cuh")
+GEMM_SOURCES = ("fp8_scaled_quantization_amd/csrc/gemm_pp.cuh", "fp8_scaled_quantization_amd/csrc/gemm_kernel.cuh",
+                "fp8_scaled_quantization_amd/csrc/gemm.hip", "fp8_scaled_quantization_amd/csrc/kernels.h",
+                "fp8_scaled_quantization_amd/csrc/common.cuh")
 
 
 def gemm_source_digest():
@@ -251,6 +256,7 @@ def main():
                 "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_FP8_TFLOPS, 4),
                 "traffic": measured_traffic() if dom == "g5" else None, "traffic_unit": "bytes per launch",
                 "avg_launch_ms": round(dom_ms, 5)}
+    next_rows = measure_next(torch, fq, o, w3, w5, args.steps)
     if args.copy_calibration:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -266,11 +272,79 @@ def main():
         "config": {"workload": WORKLOAD, "gemm_tflop_per_step": round(step_flops / 1e12, 4), "parallelism": "single GPU"},
         "pct_fp8_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
         "quantize_gbs": round(quant_gbs, 1), "quantize_pct_hbm_peak": round(100 * quant_gbs / PEAK_HBM_GBS, 2),
-        "roofline": roofline, "per_kernel": per, "input_gen_s": round(gen_s, 1),
+        "roofline": roofline, "per_kernel": per, "next_rows": next_rows, "input_gen_s": round(gen_s, 1),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(host_inputs)
     print(json.dumps(out), flush=True)
+
+
+def measure_next(torch, fq, o, w3, w5, reps):
+    """Event-timed averages (reps launches each, after one warm-up) of the next-step paths."""
+    dev = "cuda:0"
+    E4M3 = fq.E4M3
+    BLOCK, BLOCK_E8M0, TENSOR = fq.BLOCK, fq.BLOCK_E8M0, fq.TENSOR
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+
+    W5, W3, X3 = w5["W"], w3["W"], w3["X"]
+    amax = torch.zeros(1, dtype=torch.float32, device=dev)
+    state = torch.zeros(2, dtype=torch.float32, device=dev)
+    sc = torch.zeros(1, dtype=torch.float32, device=dev)
+    fq.fp8_amax(W5, amax)
+    fq.fp8_auto_scale(state, True, amax, 1e-4, E4M3, sc)
+    jit_ms = timed(lambda: (fq.fp8_amax(W5, amax), fq.fp8_auto_scale(state, True, amax, 1e-4, E4M3, sc)))
+    auto_ms = timed(lambda: fq.fp8_auto_scale(state, False, None, 1e-4, E4M3, sc))
+    h1 = torch.zeros(1024, dtype=torch.float32, device=dev)
+    h2 = torch.rand(1024, dtype=torch.float32, device=dev)
+    s1, s2 = torch.ones(1, device=dev), torch.ones(1, device=dev)
+    merge_ms = timed(lambda: fq.fp8_history_merge(h1, h2, s1, s2))
+    qw8 = torch.empty((2048, 7168), dtype=torch.uint8, device=dev)
+    ew8 = torch.empty((16, 56), dtype=torch.uint8, device=dev)
+    qe_ms = timed(lambda: fq.fp8_quantize(BLOCK_E8M0, E4M3, W3, qw8, ew8, block=(128, 128)))
+    wbf = torch.empty((2048, 7168), dtype=torch.bfloat16, device=dev)
+    dq_ms = timed(lambda: fq.fp8_block_dequantize(BLOCK_E8M0, E4M3, qw8, ew8, wbf))
+    C = o["C3"]
+    g8_ms = timed(lambda: fq.fp8_scaled_gemm(BLOCK_E8M0, o["q3x"], E4M3, o["s3x"], qw8, E4M3, ew8, None, None, C,
+                                             fq.OUT_BF16))
+    sa = torch.full((1,), float(X3.float().abs().max()) / 448.0, dtype=torch.float32, device=dev)
+    qxs = torch.empty((4096, 7168), dtype=torch.uint8, device=dev)
+    fq.fp8_quantize(TENSOR, E4M3, X3, qxs, None, sa, True)
+    gs_ms = timed(lambda: fq.fp8_scaled_gemm(BLOCK, qxs, E4M3, None, o["q3w"], E4M3, o["s3w"], sa, None, C,
+                                             fq.OUT_BF16))
+    flops = 2 * 4096 * 2048 * 7168
+    wbytes_q = 2048 * 7168 * 3 + 16 * 56
+    wbytes_dq = 2048 * 7168 * 3 + 16 * 56
+    return {
+        "auto_scale_us": round(auto_ms * 1e3, 2),
+        "jit_amax_plus_scale_us": round(jit_ms * 1e3, 2),
+        "jit_tensor": "MOSS W 4096x4096 bf16",
+        "history_merge_1024_us": round(merge_ms * 1e3, 2),
+        "ue8m0_quantize_w_2048x7168": {"ms": round(qe_ms, 5), "gbs": round(wbytes_q / (qe_ms * 1e-3) / 1e9, 1),
+                                       "pct_hbm_peak": round(100 * wbytes_q / (qe_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)},
+        "block_dequantize_ue8m0_to_bf16_2048x7168": {"ms": round(dq_ms, 5),
+                                                     "gbs": round(wbytes_dq / (dq_ms * 1e-3) / 1e9, 1),
+                                                     "pct_hbm_peak": round(100 * wbytes_dq / (dq_ms * 1e-3) / 1e9 /
+                                                                           PEAK_HBM_GBS, 2)},
+        "gemm_block_ue8m0_weights_4096x2048x7168": {"ms": round(g8_ms, 5),
+                                                    "tflops": round(flops / (g8_ms * 1e-3) / 1e12, 2),
+                                                    "pct_fp8_peak": round(100 * flops / (g8_ms * 1e-3) / 1e12 /
+                                                                          PEAK_FP8_TFLOPS, 2)},
+        "gemm_block_static_activation_4096x2048x7168": {"ms": round(gs_ms, 5),
+                                                        "tflops": round(flops / (gs_ms * 1e-3) / 1e12, 2),
+                                                        "pct_fp8_peak": round(100 * flops / (gs_ms * 1e-3) / 1e12 /
+                                                                              PEAK_FP8_TFLOPS, 2)},
+    }
 
 
 def cpu_baseline(h):
