@@ -369,6 +369,118 @@ __global__ __launch_bounds__(kTileThreads) void cast_transposed_kernel(CastArgs 
     if (FUSED_AMAX) block_reduce_atomic<NT>(cm, a.amax_out);
 }
 
+// ------------------------------------------------------------------ dual cast over band runs
+// Both copies of a bf16 tensor with rows % 128 == 0 and cols % 64 == 0, one pass.
+//
+// A workgroup walks NB consecutive 128-row bands of one 64-column strip and loads band b + 1 into
+// registers while it casts band b (two LDS tiles, one barrier per band).  Lane t holds 32
+// consecutive values of row t / 2 (columns 32 (t % 2) ..), so the row-grouped copy casts whole
+// 32-groups from registers with no cross-lane work.  For the transposed copy the two rows of a
+// pair are merged into bf16-pair words (the layout of the transposing kernel above): the lanes of
+// rows 2m and 2m + 1 (t and t ^ 2) swap half of their words with one DPP move each and every lane
+// writes 16 pair words.  Odd-row lanes load their two 16-column halves in swapped order, so that
+// the words they keep and the words they send sit in the same registers as on even-row lanes.
+//
+// The transposed copy's E8M0 bytes of the strip's 64 output rows are collected in LDS and written
+// once per run, 4 * NB contiguous bytes per output row: written band by band they are 4-byte
+// pieces of lines that workgroups on other XCDs also write, and such partial lines reach HBM
+// several times over.  Workgroup w runs on XCD w % 8 (round-robin dispatch); XCD x takes whole band
+// runs x, x + 8, ... with all their strips, so the row-grouped copy's lines and its scale lines
+// are completed inside one L2.
+template <int FMT, int MODE, bool FUSED_AMAX, bool DERIVE, int NB>
+__global__ __launch_bounds__(kTileThreads) void cast_dual_run_kernel(CastArgs a) {
+    constexpr int TC = kTileCols, NT = kTileThreads;
+    __shared__ __attribute__((aligned(16))) uint32_t tile[2][TC * 64];
+    __shared__ __attribute__((aligned(16))) uint8_t tsc[TC][4 * NB];
+    const int64_t ntx = a.cols / TC, nty = a.rows / 128, nruns = (nty + NB - 1) / NB;
+    const int64_t w = blockIdx.x, k = w / 8;
+    const int64_t run = w % 8 + 8 * (k / ntx), strip = k % ntx;
+    if (run >= nruns) return;                       // whole workgroup; no barrier reached yet
+    const UniformScale u = uniform_scale<FMT, MODE, DERIVE, true>(a);
+    const int64_t b0 = run * NB, b1 = min(nty, b0 + NB), c0 = strip * TC;
+    const int t = threadIdx.x;
+    const int rr = t >> 1, h = t & 1, odd = (t >> 1) & 1, m = t >> 2;
+    const int oc = ((t >> 5) << 3) | (t & 7), seg = (t >> 3) & 3;
+    // register slot i holds columns 32 h + 8 (i ^ 2 odd) .. + 7
+    const uint16_t* xrow = static_cast<const uint16_t*>(a.x) + (int64_t)rr * a.ld + c0 + 32 * h;
+    auto load = [&](int64_t band, uint4* v) {
+        const uint16_t* p = xrow + band * 128 * a.ld;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const uint4*>(p + 8 * (i ^ (2 * odd)));
+    };
+    // v_perm selectors: pair word = (even row value, odd row value) of one column
+    const uint32_t sel_lo = odd ? 0x01000504u : 0x05040100u, sel_hi = odd ? 0x03020706u : 0x07060302u;
+    // the 16 columns whose pair words this lane writes: 32 h + 16 odd + 0 .. 15
+    const int cw = 32 * h + 16 * odd;
+    uint4 cur[4], nxt[4];
+    load(b0, cur);
+    uint32_t tmax = 0;
+    int buf = 0;
+    for (int64_t band = b0; band < b1; ++band) {
+        // unconditional (the last band reloads itself): a conditional prefetch makes the compiler
+        // wait for every outstanding load at the top of the loop
+        load(band + 1 < b1 ? band + 1 : band, nxt);
+        uint32_t* tl = tile[buf];
+        const uint32_t wv[16] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w, cur[1].x, cur[1].y, cur[1].z, cur[1].w,
+                                 cur[2].x, cur[2].y, cur[2].z, cur[2].w, cur[3].x, cur[3].y, cur[3].z, cur[3].w};
+        // transposed copy: keep words 0..7, send words 8..15 to the partner row's lane
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)wv[8 + q], 0x4E, 0xF, 0xF, false);
+            tl[pair_word(cw + 2 * q, m)] = __builtin_amdgcn_perm(got, wv[q], sel_lo);
+            tl[pair_word(cw + 2 * q + 1, m)] = __builtin_amdgcn_perm(got, wv[q], sel_hi);
+        }
+        // row-grouped copy: one 32-group per lane
+        {
+            float v[32];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) { v[2 * q] = bf16lo(wv[q]); v[2 * q + 1] = bf16hi(wv[q]); }
+            uint32_t out[8], sc = 0, cm = 0;
+            process_chunk<FMT, MODE, true, 8>(v, u, out, sc, cm);
+            const int64_t r = band * 128 + rr;
+            uint8_t* dst = a.q2 + r * a.ldq2 + c0 + 32 * h;
+            *reinterpret_cast<uint4*>(dst + 16 * odd) = make_uint4(out[0], out[1], out[2], out[3]);
+            *reinterpret_cast<uint4*>(dst + 16 - 16 * odd) = make_uint4(out[4], out[5], out[6], out[7]);
+            if (MODE == kModeMX || MODE == kModeMoss)
+                reinterpret_cast<uint8_t*>(a.scales2)[r * (a.cols / 32) + (c0 + 32 * h) / 32] = (uint8_t)sc;
+            tmax = max(tmax, cm);
+        }
+        // one barrier per band: the other tile was last read before this barrier's previous instance
+        __syncthreads();
+        {
+            float v[32];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint4 q4 = *reinterpret_cast<const uint4*>(&tl[pair_word(oc, seg * 16 + 4 * i)]);
+                const uint32_t ww[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    v[8 * i + 2 * d] = bf16lo(ww[d]);
+                    v[8 * i + 2 * d + 1] = bf16hi(ww[d]);
+                }
+            }
+            uint32_t out[8], sc = 0, cm = 0;
+            process_chunk<FMT, MODE, true, 8>(v, u, out, sc, cm);
+            store32(a.q + (c0 + oc) * a.ldq + band * 128 + seg * 32, out);
+            if (MODE == kModeMX || MODE == kModeMoss) tsc[oc][4 * (band - b0) + seg] = (uint8_t)sc;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
+        buf ^= 1;
+    }
+    if (MODE == kModeMX || MODE == kModeMoss) {
+        __syncthreads();
+        const int nb = (int)(b1 - b0);
+        uint8_t* dst = reinterpret_cast<uint8_t*>(a.scales) + c0 * (a.rows / 32) + b0 * 4;
+        for (int i = t; i < TC * nb; i += NT) {
+            const int row = i / nb, pc = i - row * nb;
+            *reinterpret_cast<uint32_t*>(dst + row * (a.rows / 32) + pc * 4) =
+                *reinterpret_cast<const uint32_t*>(&tsc[row][pc * 4]);
+        }
+    }
+    if (FUSED_AMAX) block_reduce_atomic<NT>(tmax, a.amax_out);
+}
+
 // ------------------------------------------------------------------ 128x128 weight blocks
 // One workgroup per 128x128 block (non-transposed, rows % 128 == 0, cols % 128 == 0): thread t
 // holds row t/2, columns (t%2)*64 .. +64 in registers; block amax via LDS; one pass over HBM.
@@ -567,6 +679,24 @@ static void dual_flags(const CastArgs& a, hipStream_t st) {
     const dim3 grid((unsigned)tiles), blk(kTileThreads);
     const bool derive = a.amax_in != nullptr;
     const bool fused = a.amax_out != nullptr && MODE == kModeTensor && !derive;
+    const bool runs = BF16 && a.rows % 128 == 0 && a.cols % kTileCols == 0 && a.rows >= 32 * 128 &&
+                      ((uintptr_t)a.scales & 3) == 0;
+    if constexpr (BF16) {
+        if (runs) {
+            // runs of 16 bands from 16384 rows up, else of 4: at least 8 runs (one per XCD)
+            const int64_t nty = a.rows / 128, ntx = a.cols / kTileCols;
+            const int nb = nty >= 8 * 16 ? 16 : 4;
+            const int64_t nruns = (nty + nb - 1) / nb;
+            const dim3 g((unsigned)(((nruns + 7) / 8) * 8 * ntx));
+#define FP8Q_RUN(NBV)                                                                                              \
+            if (derive) hipLaunchKernelGGL((cast_dual_run_kernel<FMT, MODE, false, true, NBV>), g, blk, 0, st, b); \
+            else if (fused) hipLaunchKernelGGL((cast_dual_run_kernel<FMT, MODE, true, false, NBV>), g, blk, 0, st, b); \
+            else hipLaunchKernelGGL((cast_dual_run_kernel<FMT, MODE, false, false, NBV>), g, blk, 0, st, b);
+            if (nb == 16) { FP8Q_RUN(16) } else { FP8Q_RUN(4) }
+#undef FP8Q_RUN
+            return;
+        }
+    }
     if (derive) hipLaunchKernelGGL((cast_transposed_kernel<FMT, MODE, BF16, false, true, true>), grid, blk, 0, st, b);
     else if (fused) hipLaunchKernelGGL((cast_transposed_kernel<FMT, MODE, BF16, true, false, true>), grid, blk, 0, st, b);
     else hipLaunchKernelGGL((cast_transposed_kernel<FMT, MODE, BF16, false, false, true>), grid, blk, 0, st, b);

@@ -118,3 +118,45 @@ def test_dual_empty(fq):
     x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
     q, e, qt, et, S, am = fq.quantize_dual(x, MOSS, E4M3)
     assert _f32(S) == 1.0 and _f32(am) == 0.0 and q.numel() == 0 and qt.numel() == 0
+
+
+# tall bf16 operands take the band-run kernel: runs of 4, 8 (with a partial last run) and 16 bands
+RUN_SHAPES = [(4096, 64), (8576, 192), (16384, 128)]
+
+
+@pytest.mark.parametrize("rows,cols", RUN_SHAPES)
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_dual_band_runs_bit_exact(fq, orc, rows, cols, fmt):
+    xf = workloads.bf16_bits_to_f32(workloads.random_matrix(rows + 7 * cols, rows, cols, 1.0))
+    xf[:, 5] *= 60.0                                                   # an outlier channel
+    xf[rows // 3, :4] = [np.nan, np.inf, -np.inf, -0.0]                # specials in one band
+    xf[rows - 1, cols - 1] = 1e-40
+    xf[200:232, 17] = 0.0                                              # an all-zero 32-group
+    x = workloads.to_bf16_bits(xf)
+    xd = to_dev(x)
+    q, s, qt, st, S, am = fq.quantize_dual(xd, MOSS, fmt)
+    oq, oe, oS = orc.quantize_moss(x, fmt)
+    oqt, oet, _ = orc.quantize_moss(x, fmt, transpose=True)
+    assert _f32(S) == oS or (np.isnan(oS) and np.isnan(_f32(S)))
+    assert same(host(s), oe, "e") and same(host(q), oq, "q") and same(host(st), oet, "et") and same(host(qt), oqt, "qt")
+    q, s, qt, st, _, _ = fq.quantize_dual(xd, MX, fmt)
+    oq, oe = orc.quantize_mx(x, fmt)
+    oqt, oet = orc.quantize_mx(x, fmt, transpose=True)
+    assert same(host(s), oe, "e") and same(host(q), oq, "q") and same(host(st), oet, "et") and same(host(qt), oqt, "qt")
+    sd = torch.tensor([0.0123], dtype=torch.float32, device=DEV)
+    am = torch.zeros(1, dtype=torch.float32, device=DEV)
+    q, _, qt, _, _, _ = fq.quantize_dual(xd, TENSOR, fmt, tensor_scale=sd, scale_is_input=True, amax_out=am)
+    assert same(host(q), orc.quantize_tensor(x, fmt, 0.0123), "q") and \
+        same(host(qt), orc.quantize_tensor(x, fmt, 0.0123, transpose=True), "qt")
+    assert np.isnan(_f32(am)) and np.isnan(orc.amax(x))
+    xf[rows // 3, :4] = 1.0                                            # finite tensor: current scaling
+    x = workloads.to_bf16_bits(xf)
+    q, _, qt, _, S, am = fq.quantize_dual(to_dev(x), TENSOR, fmt)
+    oq, os_ = orc.quantize_tensor_current(x, fmt)
+    assert _f32(S) == os_ and _f32(am) == orc.amax(x)
+    assert same(host(q), oq, "q") and same(host(qt), orc.quantize_tensor(x, fmt, os_, transpose=True), "qt")
+    q, s, qt, st, S, _ = fq.quantize_dual(to_dev(x), MOSS, fmt)
+    oq, oe, oS = orc.quantize_moss(x, fmt)
+    oqt, oet, _ = orc.quantize_moss(x, fmt, transpose=True)
+    assert _f32(S) == oS
+    assert same(host(s), oe, "e") and same(host(q), oq, "q") and same(host(st), oet, "et") and same(host(qt), oqt, "qt")

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 from fp8_scaled_quantization_amd import workloads
-from tests.gpu_util import DEV, check_gemm, chunk_max_sum, host, same, sample_pairs, to_dev
+from tests.gpu_util import DEV, chain_prefix_abs, check_gemm, chunk_max_sum, host, same, sample_pairs, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -214,3 +214,54 @@ def test_block_gemm_weight_and_activation_scale_kinds(fq, orc, wmode, static_a, 
 @pytest.mark.parametrize("wmode,static_a", [(BLOCK_E8M0, False), (BLOCK, True), (BLOCK_E8M0, True)])
 def test_block_gemm_fine_grained_full_size_sampled(fq, orc, wmode, static_a):
     _gemm_case(fq, orc, 4096, 2048, 7168, wmode, static_a, 3, sampled=True)
+
+
+# ------------------------------------------------------------------ delayed-scaling backward
+def test_delayed_forward_backward_steps(fq, orc):
+    """A linear layer trained with delayed scaling: three delayed states (input and kernel in E4M3,
+    output gradient in E5M2) drive Y = X W^T, dX = dY W and dW = dY^T X ("Flax FP8 量化实战指南 ...",
+    section 3.3: the backward quantizes the incoming gradient to E5M2 under its own state).  Each
+    operand is quantized once into both layouts (post-step history updates), and every byte,
+    amax, history and scale equals the oracle's in-step replay; the GEMMs are within the bound."""
+    M, I, O, L = 640, 384, 256, 1024
+    fmts = {"x": E4M3, "w": E4M3, "g": E5M2}
+    dev_st = {k: (torch.ones(1, dtype=torch.float32, device=DEV), torch.zeros(L, dtype=torch.float32, device=DEV))
+              for k in fmts}
+    orc_st = {k: (np.ones(1, np.float32), np.zeros(L, np.float32)) for k in fmts}
+    W0 = workloads.bf16_bits_to_f32(workloads.random_matrix(900, O, I, 0.02))
+    for t in range(6):
+        rng = np.random.default_rng(1000 + t)
+        sig = np.float32(np.exp(rng.uniform(np.log(0.1), np.log(10.0))))
+        raw = {"x": workloads.random_matrix(1100 + t, M, I, float(sig)),
+               "w": workloads.to_bf16_bits(W0 + workloads.bf16_bits_to_f32(workloads.random_matrix(1200 + t, O, I, 1e-4))),
+               "g": workloads.random_matrix(1300 + t, M, O, float(1e-3 * sig))}
+        if t == 4:
+            raw["g"] = np.zeros_like(raw["g"])          # an all-zero gradient keeps the previous scale
+        dq, oq, used = {}, {}, {}
+        for k, fmt in fmts.items():
+            scale, hist = dev_st[k]
+            amax = torch.zeros(1, dtype=torch.float32, device=DEV)
+            q, _, qt, _, _, _ = fq.quantize_dual(to_dev(raw[k]), TENSOR, fmt, tensor_scale=scale,
+                                                 scale_is_input=True, amax_out=amax)
+            osc, ohist = orc_st[k]
+            oq_rows, oa = orc.delayed_step(raw[k], fmt, osc, ohist)
+            oq_cols = orc.quantize_tensor(raw[k], fmt, osc[0], transpose=True)
+            assert np.float32(host(amax)[0]) == oa, (t, k)
+            assert same(host(q), oq_rows, "%s rows t=%d" % (k, t)) and same(host(qt), oq_cols, "%s cols t=%d" % (k, t))
+            used[k] = np.float32(osc[0])
+            dq[k] = (q, qt, scale.clone())
+            oq[k] = (oq_rows, oq_cols)
+            fq.fp8_history_update(hist, amax, scale, fmt)
+            nxt = orc.compute_scale(orc.history_max(ohist), fmt, osc[0])
+            assert np.array_equal(host(hist), ohist) and np.float32(host(scale)[0]) == nxt, (t, k)
+        deq = lambda k, which: orc.dequantize(TENSOR, oq[k][which], fmts[k], None, used[k])
+        cases = (("Y", ("x", 0), ("w", 0), I), ("dX", ("g", 0), ("w", 1), O), ("dW", ("g", 1), ("x", 1), M))
+        for name, (ka, wa), (kb, wb), K in cases:
+            C32 = fq.scaled_gemm(TENSOR, dq[ka][wa], fmts[ka], None, dq[kb][wb], fmts[kb], None,
+                                 dq[ka][2], dq[kb][2], out_dtype=OUT_F32)
+            Cbf = fq.scaled_gemm(TENSOR, dq[ka][wa], fmts[ka], None, dq[kb][wb], fmts[kb], None,
+                                 dq[ka][2], dq[kb][2], out_dtype=OUT_BF16)
+            Ad, Bd = deq(ka, wa), deq(kb, wb)
+            Cref, D = orc.gemm_ref(Ad, Bd)
+            check_gemm(host(C32), host(Cbf), Cref, D, chunk_max_sum(Ad, Bd), K, "%s t=%d" % (name, t),
+                       chain_prefix_abs(Ad, Bd))
