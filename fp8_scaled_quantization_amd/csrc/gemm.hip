@@ -30,6 +30,7 @@
 #include "common.cuh"
 #include "gemm_kernel.cuh"
 #include "gemm_pp.cuh"
+#include "gemm_ppb.cuh"
 #include "kernels.h"
 
 namespace fp8q {
@@ -261,6 +262,30 @@ static void launch_v2(const GemmArgs& g, hipStream_t st) {
 }
 
 // Ping-pong kernel (gemm_pp.cuh): TENSOR, MX and MOSS with K % 128 == 0.
+// Ping-pong block-scaled kernel (gemm_ppb.cuh): BLOCK / BLOCK_E8M0 with K % 128 == 0.
+template <int AFMT, int BFMT, bool OUT, bool E8, bool AST>
+static void launch_ppb_k(const GemmArgs& g, hipStream_t st) {
+    const int64_t ntm = (g.M + ppb::BM - 1) / ppb::BM, ntn = (g.N + ppb::BN - 1) / ppb::BN;
+    auto kern = ppb::gemm_ppb_kernel<AFMT, BFMT, OUT, E8, AST>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)ppb::kLdsBytes);
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)(ntm * ntn)), dim3(512), ppb::kLdsBytes, st, g);
+}
+template <int AFMT, int BFMT, bool OUT>
+static void launch_ppb(const GemmArgs& g, hipStream_t st) {
+    if (g.b_e8m0) {
+        if (g.a_static) launch_ppb_k<AFMT, BFMT, OUT, true, true>(g, st);
+        else launch_ppb_k<AFMT, BFMT, OUT, true, false>(g, st);
+    } else {
+        if (g.a_static) launch_ppb_k<AFMT, BFMT, OUT, false, true>(g, st);
+        else launch_ppb_k<AFMT, BFMT, OUT, false, false>(g, st);
+    }
+}
+
 template <int MODE, int AFMT, int BFMT, bool OUT>
 static void launch_pp(const GemmArgs& g, hipStream_t st) {
     const int64_t ntm = (g.M + pp::BM - 1) / pp::BM, ntn = (g.N + pp::BN - 1) / pp::BN;
@@ -285,8 +310,8 @@ static void launch_sel(const GemmArgs& g, hipStream_t st) {
         return;
     }
     if constexpr (MODE == kModeBlock) {
-        // per-128 promotion with the block scales: 256 x 128 tiles, 8 waves of 64 x 64
-        launch_v2<MODE, AFMT, BFMT, OUT, 256, 128, 4, 2, 3>(g, st);
+        // per-128 promotion with the block scales: the ping-pong kernel's 256 x 128 tiles
+        launch_ppb<AFMT, BFMT, OUT>(g, st);
     } else {
         // whole-K accumulation on the matrix cores: the ping-pong kernel's 256 x 256 tiles when
         // there are enough of them to fill the GPU; 128 x 128 tiles otherwise

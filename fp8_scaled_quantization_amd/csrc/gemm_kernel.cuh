@@ -3,12 +3,10 @@
 // Scale handling per scheme (same arithmetic as the reference-tile kernel in gemm.hip):
 //   TENSOR  C = (sum qa*qb) * fl(s_a*s_b) in the epilogue (page "Flax FP8 量化实战指南 ...",
 //           section 2.2);
-//   BLOCK   each 128-wide K block's FP32 partial is scaled by fl(sx[m][kb] * sw[n/128][kb]) and
-//           accumulated in the main loop (page "Transformers 中的细粒度 FP8 量化配置 ...", section 一);
-//           sw may be an E8M0 power of two (section 七) and sx one static per-tensor activation
-//           scale (section 四);
 //   MX/MOSS E8M0 scales per 32-wide K group applied by v_mfma_scale_f32_16x16x128_f8f6f4; MOSS adds
 //           fl(S_A*S_B) in the epilogue (page "MOSS:高效、精确的 FP8 LLM 训练 ...", sections 1, 4).
+// Block scaling, which promotes every K step, has its own kernel (gemm_ppb.cuh).  The helpers
+// below (descriptors, copies, waits, uniform loads) are shared with it and with gemm_pp.cuh.
 //
 // Data movement.  A and B K-tiles (128 bytes of K per row) go from HBM straight into LDS with
 // buffer_load_dwordx4 ... lds: no VGPR staging, and rows past M or N read as zero through the
@@ -17,13 +15,12 @@
 // chunk position c ^ (r & 7), so both the DMA writes (8 rows per wave instruction) and the MFMA
 // fragment reads are bank-conflict free; the swizzle is applied by choosing which global chunk
 // each lane fetches.  Per-row scales travel in 16-byte quads that cover four K steps (16 E8M0
-// bytes, or 4 fp32 block scales), loaded every fourth step into a two-entry ring, so each wave
+// bytes), loaded every fourth step into a two-entry ring, so each wave
 // instruction fetches four steps' worth of the 64 rows it touches.
 //
 // Accumulation.  The FP8 MFMA keeps only ~12-15 bits below the largest term it adds (its
 // products and its C input).  TENSOR, MX and MOSS keep the whole K sum in the instruction's FP32
-// accumulator, as the MOSS page's design keeps the main loop on the matrix cores; BLOCK computes
-// each 128-wide step from zero and promotes it into VGPR FP32 accumulators with its block scale.
+// accumulator, as the MOSS page's design keeps the main loop on the matrix cores.
 //
 // MFMA operand layout for 16x16x128 (lane l = r + 16 g): bytes 0-15 hold A[r][16g .. 16g+15],
 // bytes 16-31 hold A[r][64+16g .. 64+16g+15]; the E8M0 scale of (row r, 32-group q) is taken from
@@ -115,7 +112,7 @@ template <int MODE, int BM, int BN, int STAGES>
 struct Layout {
     static constexpr bool SCALED = MODE == kModeMX || MODE == kModeMoss;
     static constexpr int kA = BM * BK, kB = BN * BK, kStage = kA + kB;
-    static constexpr int kScRows = MODE == kModeTensor ? 0 : (SCALED ? BM + BN : BM);
+    static constexpr int kScRows = SCALED ? BM + BN : 0;
     static constexpr int kScQuad = kScRows * 16;              // one scale quad (4 K steps)
     static constexpr int kScBase = STAGES * kStage;
     static constexpr int kBytes = kScBase + 2 * kScQuad;
@@ -137,16 +134,19 @@ __device__ __forceinline__ void issue_step(uint8_t* smem, int64_t kt, int wave, 
     for (int j = 0; j < B_LD; ++j) dma16(lds_addr(st + L::kA + (wave * B_LD + j) * 8 * BK), rb, offB[j], koff);
     if (L::kScRows > 0 && kt % SQ == 0) {
         uint8_t* sq = smem + L::kScBase + ((kt / SQ) & 1) * L::kScQuad;
-        const uint32_t soff = (uint32_t)(kt * 4);     // 4 scale bytes per K step
+        // 4 scale bytes per K step.  The K offset goes into the range-checked lane offset: with K
+        // steps not a multiple of 4 the last quad of a row ends past the row, and on the array's
+        // last row past its end, where the buffer range turns the excess into zeros.
+        const uint32_t kq = (uint32_t)(kt * 4);
 #pragma unroll
         for (int j = 0; j < SC_LD_TOTAL; ++j) {
             if (wave == j % NW) {
                 const bool isA = j * 64 < BM;
                 const int rowb = isA ? j * 64 : j * 64 - BM;
-                const uint32_t off = (uint32_t)((rowb + lane) * sc_row);
+                const uint32_t off = (uint32_t)((rowb + lane) * sc_row) + kq;
                 uint8_t* dst = sq + (isA ? 0 : BM * 16) + rowb * 16;
-                if (isA) dma16(lds_addr(dst), rsa, off, soff);
-                else dma16(lds_addr(dst), rsb, off, soff);
+                if (isA) dma16(lds_addr(dst), rsa, off, 0u);
+                else dma16(lds_addr(dst), rsb, off, 0u);
             }
         }
     }
@@ -159,8 +159,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmArgs g
     constexpr int TM = WTM / 16, TN = WTN / 16;
     using L = Layout<MODE, BM, BN, STAGES>;
     constexpr bool SCALED = L::SCALED;
-    constexpr bool BLOCKED = MODE == kModeBlock;
-    static_assert(!BLOCKED || BN == 128, "block-scaled B tiles must match the 128-row weight blocks");
+    static_assert(MODE == kModeTensor || SCALED, "block scaling has its own kernel (gemm_ppb.cuh)");
     // 16-byte chunk loads per stage: (BM + BN) rows x 8 chunks; one wave instruction = 8 rows
     constexpr int A_LD = BM / 8 / NW, B_LD = BN / 8 / NW;
     static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile/wave split");
@@ -192,25 +191,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmArgs g
     const int64_t m0 = (first_m + in_grp % gm) * BM, n0 = (in_grp / gm) * BN;
 
     const int64_t nk = K / BK;
-    const int64_t nkb = K / 128;
 
     // ---- buffer descriptors (ranges end at the last row, so rows >= M / N read zero)
     const rsrc_t ra = make_rsrc(g.A + m0 * g.lda, (uint32_t)(max((int64_t)0, M - m0) * g.lda));
     const rsrc_t rb = make_rsrc(g.B + n0 * g.ldb, (uint32_t)(max((int64_t)0, N - n0) * g.ldb));
-    // per-row scale bytes: MX/MOSS one E8M0 per 32-group, BLOCK one fp32 per 128 block -- either
-    // way 4 bytes per K step
+    // per-row scale bytes: one E8M0 per 32-group, 4 bytes per K step
     const int64_t sc_row = 4 * nk;
     const uint8_t* sca_base = static_cast<const uint8_t*>(g.Ascale);
     const uint8_t* scb_base = static_cast<const uint8_t*>(g.Bscale);
     uint32_t sca_bytes = 0, scb_bytes = 0;
-    if (SCALED || (BLOCKED && !g.a_static)) {
+    if (SCALED) {
         sca_base += m0 * sc_row;
         sca_bytes = (uint32_t)(max((int64_t)0, M - m0) * sc_row);
-    }
-    // static activation scale (BLOCK with one per-tensor activation scale): the per-row scale
-    // quads read as zeros (empty buffer range) and the tensor scale stands in for them
-    const float a_static = (BLOCKED && g.a_static) ? load_uniform_f32(g.Aglobal) : 0.0f;
-    if (SCALED) {
         scb_base += n0 * sc_row;
         scb_bytes = (uint32_t)(max((int64_t)0, N - n0) * sc_row);
     }
@@ -290,8 +282,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmArgs g
             scb[j] = 0;
             if (SCALED) scb[j] = (int)((sqB[(wn * WTN + j * 16 + r16) * 4 + qs] >> (8 * g4)) & 0xFFu);
         }
-        float sw = 1.0f;
-        if (BLOCKED) sw = weight_block_scale(g, (n0 / 128) * nkb + kt);
 
         // A fragments: the next subtile's reads are issued before this subtile's MFMAs
         v8i fa_next;
@@ -312,30 +302,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmArgs g
                 fa_next = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                 if (SCALED) sca_next = (int)((sqA[(wm * WTM + (i + 1) * 16 + r16) * 4 + qs] >> (8 * g4)) & 0xFFu);
             }
-            if constexpr (BLOCKED) {
-                float rs[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    rs[e] = (g.a_static ? a_static : __uint_as_float(sqA[(wm * WTM + i * 16 + 4 * g4 + e) * 4 + qs])) * sw;
-                v4f p[TN];
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb[j], v4f{0.f, 0.f, 0.f, 0.f}, AFMT, BFMT,
-                                                                            0, 0, 0, 0);
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(rs[e], p[j][e], acc[i][j][e]);
-            } else {
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    if (SCALED)
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb[j], acc[i][j], AFMT, BFMT, 0, sca,
-                                                                                      0, scb[j]);
-                    else
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb[j], acc[i][j], AFMT, BFMT, 0, 0,
-                                                                                      0, 0);
-                }
+            for (int j = 0; j < TN; ++j) {
+                if (SCALED)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb[j], acc[i][j], AFMT, BFMT, 0, sca, 0,
+                                                                                  scb[j]);
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb[j], acc[i][j], AFMT, BFMT, 0, 0, 0, 0);
             }
         }
     }

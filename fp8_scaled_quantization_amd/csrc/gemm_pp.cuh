@@ -75,6 +75,24 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
+// Full-tile bf16 epilogue piece: a 4x4 transpose of bf16 values within each quad of lanes turns
+// the MFMA layout (lane r16 holds one column, four rows of a 16 x 16 subtile) into one row and four
+// columns per lane: lane (g4, r16 = 4 c4 + q) gets row 4 g4 + q, columns 4 c4 .. 4 c4 + 3, which it
+// stores with one 8-byte write (each row's 32 bytes come from four lanes).  modd and mhi are the
+// lane-constant masks 0 - (q & 1) and 0 - (q >> 1): the selections are bit selects, not branches.
+__device__ __forceinline__ uint2 quad_transpose_bf16(v4f v, uint32_t modd, uint32_t mhi) {
+    const uint32_t w0 = pack_bf16(v[0], v[1]), w1 = pack_bf16(v[2], v[3]);   // rows (0,1), (2,3)
+    // swap with lane q^1: even lanes collect rows 0 and 2, odd lanes rows 1 and 3, of two adjacent
+    // columns
+    const uint32_t s1 = bitsel(modd, (w0 & 0xFFFFu) | (w1 << 16), (w0 >> 16) | (w1 & 0xFFFF0000u));
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s1, 0xB1, 0xF, 0xF, false);   // [1,0,3,2]
+    const uint32_t x0 = bitsel(modd, (r1 & 0xFFFFu) | (w0 & 0xFFFF0000u), (w0 & 0xFFFFu) | (r1 << 16));
+    const uint32_t x1 = bitsel(modd, (r1 >> 16) | (w1 & 0xFFFF0000u), (w1 & 0xFFFFu) | (r1 & 0xFFFF0000u));
+    // swap with lane q^2: lane q ends with row q, columns 0-1 and 2-3 of the quad
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)bitsel(mhi, x0, x1), 0x4E, 0xF, 0xF, false);   // [2,3,0,1]
+    return make_uint2(bitsel(mhi, r2, x0), bitsel(mhi, x1, r2));
+}
+
 __device__ __forceinline__ v8i frag(const uint8_t* row, uint32_t lo, uint32_t hi) {
     const uint4 a = *reinterpret_cast<const uint4*>(row + lo);
     const uint4 b = *reinterpret_cast<const uint4*>(row + hi);
@@ -130,15 +148,18 @@ __device__ __forceinline__ void copy_B(uint8_t* smem, int s, int base, int wi, r
     }
 }
 // Group 0, wave wi, every fourth step: two instructions of the scale quad for steps s .. s+3.
+// The K offset goes into the range-checked lane offset: when the K steps are not a multiple of 4
+// the last quad of a row ends past the row, and on the array's last row past its end, where the
+// buffer range turns the excess into zeros.
 __device__ __forceinline__ void copy_quad(uint8_t* smem, int s, int wi, rsrc_t rsa, rsrc_t rsb, uint32_t voffS,
                                           uint32_t sc_row) {
     uint8_t* sq = smem + kScBase + ((s >> 2) & 1) * kScQuad;
-    const uint32_t soff = (uint32_t)s * 4;
+    const uint32_t voff = voffS + (uint32_t)s * 4;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int inst = wi * 2 + j;              // 0..3: A rows, 4..7: B rows, 64 rows each
         const uint32_t r0 = (uint32_t)(inst & 3) * 64;
-        copy8(sq + inst * 64 * 16, inst < 4 ? rsa : rsb, voffS, r0 * sc_row, soff);
+        copy8(sq + inst * 64 * 16, inst < 4 ? rsa : rsb, voff, r0 * sc_row, 0u);
     }
 }
 
@@ -343,13 +364,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
     // ---- epilogue
     const float f = (MODE == kModeTensor || MODE == kModeMoss) ? ga * gb : 1.0f;
     if (OUT_BF16 && m0 + BM <= M && n0 + BN <= N) {
-        // Full tile.  A 4x4 transpose of bf16 values within each quad of lanes turns the MFMA
-        // layout (lane r16 holds one column, four rows) into one row and four columns per lane:
-        // lane (g4, r16 = 4 c4 + q) then holds row 4 g4 + q, columns 4 c4 .. 4 c4 + 3 of a 16 x 16
-        // subtile, stored with one 8-byte write (each row's 32 bytes come from four lanes).
+        // full tile: quad transposes and 8-byte stores (quad_transpose_bf16)
         const int q = r16 & 3, c4 = r16 >> 2;
-        // lane-constant masks (all ones for odd q / for q >= 2): selections are bit selects,
-        // not branches
         const uint32_t modd = 0u - (uint32_t)(q & 1), mhi = 0u - (uint32_t)(q >> 1);
         uint16_t* const cw = static_cast<uint16_t*>(g.C) + (m0 + wm * 64) * g.ldc + n0 + wn * 128;
         const uint32_t loff = (uint32_t)((4 * g4 + q) * g.ldc + 4 * c4);
@@ -357,20 +373,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
         for (int i = 0; i < 4; ++i) {
             uint16_t* const ci = cw + (int64_t)i * 16 * g.ldc;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const v4f v = acc[i][j] * f;
-                const uint32_t w0 = pack_bf16(v[0], v[1]), w1 = pack_bf16(v[2], v[3]);   // rows (0,1), (2,3)
-                // swap with lane q^1: even lanes collect rows 0 and 2, odd lanes rows 1 and 3, of
-                // two adjacent columns
-                const uint32_t s1 = bitsel(modd, (w0 & 0xFFFFu) | (w1 << 16), (w0 >> 16) | (w1 & 0xFFFF0000u));
-                const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s1, 0xB1, 0xF, 0xF, false);   // [1,0,3,2]
-                const uint32_t x0 = bitsel(modd, (r1 & 0xFFFFu) | (w0 & 0xFFFF0000u), (w0 & 0xFFFFu) | (r1 << 16));
-                const uint32_t x1 = bitsel(modd, (r1 >> 16) | (w1 & 0xFFFF0000u), (w1 & 0xFFFFu) | (r1 & 0xFFFF0000u));
-                // swap with lane q^2: lane q ends with row q, columns 0-1 and 2-3 of the quad
-                const uint32_t r2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)bitsel(mhi, x0, x1), 0x4E, 0xF, 0xF, false);   // [2,3,0,1]
-                const uint2 d = make_uint2(bitsel(mhi, r2, x0), bitsel(mhi, x1, r2));
-                *reinterpret_cast<uint2*>(ci + loff + j * 16) = d;
-            }
+            for (int j = 0; j < 8; ++j)
+                *reinterpret_cast<uint2*>(ci + loff + j * 16) = quad_transpose_bf16(acc[i][j] * f, modd, mhi);
         }
     } else {
         // partial tile or fp32 output: element by element, masked

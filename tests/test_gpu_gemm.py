@@ -46,7 +46,7 @@ def _run(fq, mode, A, afmt, B, bfmt, out):
     return fq.scaled_gemm(mode, qa, afmt, sa, qb, bfmt, sb, ga, gb, out_dtype=out)
 
 
-SMALL = [(200, 136, 384), (128, 128, 128), (256, 384, 1024), (16, 64, 32), (300, 260, 272)]
+SMALL = [(200, 136, 384), (128, 128, 128), (256, 384, 1024), (16, 64, 32), (300, 260, 272), (600, 400, 1152)]
 
 
 @pytest.mark.parametrize("mode", [TENSOR, BLOCK, MX, MOSS])
