@@ -262,27 +262,32 @@ static void launch_v2(const GemmArgs& g, hipStream_t st) {
 }
 
 // Ping-pong kernel (gemm_pp.cuh): TENSOR, MX and MOSS with K % 128 == 0.
-// Ping-pong block-scaled kernel (gemm_ppb.cuh): BLOCK / BLOCK_E8M0 with K % 128 == 0.
-template <int AFMT, int BFMT, bool OUT, bool E8, bool AST>
+// Ping-pong kernel with 256 x 128 tiles (gemm_ppb.cuh): every BLOCK / BLOCK_E8M0 problem, and
+// TENSOR/MX/MOSS problems too small for the 256 x 256 tiles.  K % 128 == 0.
+template <int MODE, int AFMT, int BFMT, bool OUT, bool E8, bool AST>
 static void launch_ppb_k(const GemmArgs& g, hipStream_t st) {
     const int64_t ntm = (g.M + ppb::BM - 1) / ppb::BM, ntn = (g.N + ppb::BN - 1) / ppb::BN;
-    auto kern = ppb::gemm_ppb_kernel<AFMT, BFMT, OUT, E8, AST>;
+    auto kern = ppb::gemm_ppb_kernel<MODE, AFMT, BFMT, OUT, E8, AST>;
+    constexpr size_t smem = ppb::lds_bytes<MODE>();
     static bool attr_set = false;
     if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)ppb::kLdsBytes);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)(ntm * ntn)), dim3(512), ppb::kLdsBytes, st, g);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(ntm * ntn)), dim3(512), smem, st, g);
 }
-template <int AFMT, int BFMT, bool OUT>
+template <int MODE, int AFMT, int BFMT, bool OUT>
 static void launch_ppb(const GemmArgs& g, hipStream_t st) {
-    if (g.b_e8m0) {
-        if (g.a_static) launch_ppb_k<AFMT, BFMT, OUT, true, true>(g, st);
-        else launch_ppb_k<AFMT, BFMT, OUT, true, false>(g, st);
+    if constexpr (MODE == kModeBlock) {
+        if (g.b_e8m0) {
+            if (g.a_static) launch_ppb_k<MODE, AFMT, BFMT, OUT, true, true>(g, st);
+            else launch_ppb_k<MODE, AFMT, BFMT, OUT, true, false>(g, st);
+        } else {
+            if (g.a_static) launch_ppb_k<MODE, AFMT, BFMT, OUT, false, true>(g, st);
+            else launch_ppb_k<MODE, AFMT, BFMT, OUT, false, false>(g, st);
+        }
     } else {
-        if (g.a_static) launch_ppb_k<AFMT, BFMT, OUT, false, true>(g, st);
-        else launch_ppb_k<AFMT, BFMT, OUT, false, false>(g, st);
+        launch_ppb_k<MODE, AFMT, BFMT, OUT, false, false>(g, st);
     }
 }
 
@@ -311,12 +316,14 @@ static void launch_sel(const GemmArgs& g, hipStream_t st) {
     }
     if constexpr (MODE == kModeBlock) {
         // per-128 promotion with the block scales: the ping-pong kernel's 256 x 128 tiles
-        launch_ppb<AFMT, BFMT, OUT>(g, st);
+        launch_ppb<MODE, AFMT, BFMT, OUT>(g, st);
     } else {
         // whole-K accumulation on the matrix cores: the ping-pong kernel's 256 x 256 tiles when
-        // there are enough of them to fill the GPU; 128 x 128 tiles otherwise
+        // there are enough of them to fill the GPU, else its 256 x 128 tiles, else 128 x 128 tiles
         const int64_t big_tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256);
+        const int64_t mid_tiles = ((g.M + 255) / 256) * ((g.N + 127) / 128);
         if (big_tiles >= 192) launch_pp<MODE, AFMT, BFMT, OUT>(g, st);
+        else if (mid_tiles >= 192) launch_ppb<MODE, AFMT, BFMT, OUT>(g, st);
         else launch_v2<MODE, AFMT, BFMT, OUT, 128, 128, 2, 2, 3>(g, st);
     }
 }

@@ -170,7 +170,9 @@ def test_gemm_moss_forward_backward_full_size_sampled(fq, orc):
 
 # Shapes with enough 256 x 256 tiles (>= 192) to take the ping-pong kernel, with partial tiles in
 # M and N and K of one, two and five 128-wide steps (the copy pipeline's start-up and drain cases).
-PINGPONG = [(3000, 4000, 128), (3000, 4000, 256), (2900, 4100, 640)]
+# 256 x 256 ping-pong kernel (at least 192 tiles of 256 x 256), then the 256 x 128 one (fewer, but at
+# least 192 tiles of 256 x 128), with partial tiles and a partial last scale quad
+PINGPONG = [(3000, 4000, 128), (3000, 4000, 256), (2900, 4100, 640), (2900, 2100, 640), (4096, 2048, 1152)]
 
 
 @pytest.mark.parametrize("mode", [TENSOR, MX, MOSS])
