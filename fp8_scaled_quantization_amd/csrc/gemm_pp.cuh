@@ -20,12 +20,18 @@
 // but reads A of step k during its compute phase for step k-1 (also phase 2k), one 16-row A block
 // right after the last MFMA that used the previous step's block, so it needs no extra registers.
 // A and B0 of a stage are therefore free one phase after they are first read, and every copy gets
-// about two and a half phases to land:
-//   A, B0 of step k+2 (and the scale quad of a quad's first step)
+// about two phases to land:
+//   A of step k+2 (and the scale quad of a quad's first step)
 //                 group 1, memory phase for step k (phase 2k+1), waited at the end of phase 2k+3;
+//   B0 of step k+2  group 0, after the MFMAs of its compute phase for step k (phase 2k+1), waited at
+//                 the end of phase 2k+3;
 //   B1 of step k+1  group 0, memory phase for step k (phase 2k),   waited at the end of phase 2k+2.
-// Copies are issued only in memory phases, interleaved with the fragment reads: a copy instruction
-// can hold its wave while the address unit is busy, which must not delay that wave's MFMAs.
+// A copy instruction can hold its wave while the address unit is busy, so copies never sit between
+// a wave's MFMAs: group 1 interleaves its eight with its fragment reads, group 0 sends its B1 copies
+// among its fragment reads and its B0 copies after its MFMAs.  (Measured with per-phase timestamps:
+// with all twelve A and B0 copies in group 1's memory phase, that phase took ~1470 cycles against
+// ~1190 for group 0's compute phase, and the matrix core idled for the difference; with the B0
+// copies moved, a K step takes ~3000 cycles instead of ~3150.)
 //
 // Global->LDS copies use buffer_load_dwordx4 ... lds (no VGPR staging; rows past M or N read zero
 // through the buffer range), with each 16-byte chunk c of tile row r stored at chunk position
@@ -280,36 +286,30 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
                     if (q < 4) fa[q] = frag(sa + rowA + q * 16 * BK, cLo, cHi);
                     else fb[q - 4] = frag(sb + rowB + (q - 4) * 16 * BK, cLo, cHi);
                 }
-                // B1 of step k (sent one memory phase ago) lands before group 1 reads it next phase
-                if (cp) wait_vm<4>();
+                // B1 of step k (sent one memory phase ago) lands before group 1 reads it next phase;
+                // newer: B0 of step k+1 (sent in the last compute phase) and this phase's B1
+                if (cp && k >= 1) wait_vm<8>();
+                else if (cp) wait_vm<4>();
                 else wait_vm0();
             } else {
-                // B1 of step k; A and B0 of step k+2 (8 + 4 copies) and the scale quad
+                // B1 of step k; A of step k+2 (8 copies, one per fragment read) and the scale quad
                 const bool cp = k + 2 < nk;
                 uint8_t* st = smem + (k & 1) * kStage;
                 const uint32_t koff = (uint32_t)(k + 2) * BK;
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
                     if (cp) {
-#pragma unroll
-                        for (int c = (q < 4 ? 2 * q : q + 4); c < (q < 4 ? 2 * q + 2 : q + 5); ++c) {
-                            if (c < 8) {
-                                const uint32_t r0 = (uint32_t)(wi * 64 + c * 8);
-                                copy8(st + r0 * BK, ra, voffA, r0 * ulda, koff);
-                            } else {
-                                const uint32_t r0 = (uint32_t)(wi * 32 + (c - 8) * 8);
-                                copy8(st + kA + r0 * BK, rb, voffB, r0 * uldb, koff);
-                            }
-                        }
+                        const uint32_t r0 = (uint32_t)(wi * 64 + q * 8);
+                        copy8(st + r0 * BK, ra, voffA, r0 * ulda, koff);
                     }
                     fb[q] = frag(sb + rowB + q * 16 * BK, cLo, cHi);
                 }
                 const bool quad = SCALED && cp && ((k + 2) & 3) == 0;
                 if (quad) copy_quad(smem, k + 2, wi, rsa, rsb, voffS, usc);
-                // A and B0 of step k+1 (sent one memory phase ago) land before group 0 reads them
-                // next phase; this phase's copies may stay in flight
-                if (quad) wait_vm<14>();
-                else if (cp) wait_vm<12>();
+                // A of step k+1 (sent one memory phase ago) lands before group 0 reads it next
+                // phase; this phase's copies may stay in flight
+                if (quad) wait_vm<10>();
+                else if (cp) wait_vm<8>();
                 else wait_vm0();
             }
         }
@@ -357,6 +357,24 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
         for (int i = 0; i < 4; ++i)
             asm volatile("" ::"v"(acc[i][0]), "v"(acc[i][1]), "v"(acc[i][2]), "v"(acc[i][3]), "v"(acc[i][4]),
                          "v"(acc[i][5]), "v"(acc[i][6]), "v"(acc[i][7]));
+        if (grp == 0) {
+            // B0 of step k+2, into the stage group 0 finished reading last phase, sent after this
+            // phase's MFMAs: group 1's memory phase, which moves A, is the longer one
+            if (k + 2 < nk) {
+                uint8_t* st = smem + (k & 1) * kStage + kA;
+                const uint32_t koff = (uint32_t)(k + 2) * BK;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t r0 = (uint32_t)(wi * 32 + j * 8);
+                    copy8(st + r0 * BK, rb, voffB, r0 * uldb, koff);
+                }
+            }
+            // B0 of step k+1 (sent in the last compute phase) lands before group 0 reads it next
+            // phase; newer: B1 of step k+1 (this memory phase) and B0 of step k+2
+            if (k + 2 < nk) wait_vm<8>();
+            else if (k + 1 < nk) wait_vm<4>();
+            else wait_vm0();
+        }
         barrier();
     }
     if (grp == 0) barrier();          // matches group 1's extra barrier at the start
