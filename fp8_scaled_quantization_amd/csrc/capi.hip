@@ -118,6 +118,13 @@ int fp8_quantize(int mode, int fmt, const void* x, int in_dtype, int64_t rows, i
     a.block_r = block_r;
     a.block_c = block_c;
     a.vec_out = ldq % 16 == 0 && aligned16(q);
+    if (mode == FP8Q_TENSOR && needs_amax && !empty && rows * cols <= fp8q::kSmallCastElems) {
+        // small tensor: amax, scale and cast in one launch
+        a.amax_out = amax_out;
+        a.scale_out = tensor_scale;
+        fp8q::launch_cast_small_current(a, st);
+        return check_launch("fp8_quantize");
+    }
     if (mode == FP8Q_TENSOR || mode == FP8Q_MOSS) {
         if (needs_amax) {
             fp8q::launch_amax(x, bf16, rows, cols, ld, amax_out, st);
@@ -199,6 +206,13 @@ int fp8_quantize_dual(int mode, int fmt, const void* x, int in_dtype, int64_t ro
     a.ldq2 = ldq;
     a.scales2 = scales;
     a.vec_out = true;
+    if (mode == FP8Q_TENSOR && needs_amax && !empty && rows * cols <= fp8q::kSmallCastElems) {
+        // small tensor: amax, scale and both copies in one launch
+        a.amax_out = amax_out;
+        a.scale_out = tensor_scale;
+        fp8q::launch_cast_small_current(a, st);
+        return check_launch("fp8_quantize_dual");
+    }
     if (mode == FP8Q_TENSOR || mode == FP8Q_MOSS) {
         if (needs_amax) {
             fp8q::launch_amax(x, bf16, rows, cols, ld, amax_out, st);

@@ -43,6 +43,11 @@ int launch_cast_dual(const CastArgs& a, hipStream_t st);
 // Casts with the tensor scale (or S) either given (scale_in) or derived from amax_in.
 int launch_cast(const CastArgs& a, hipStream_t st);
 
+// Per-tensor current scaling (TENSOR, scale derived) of a tensor of at most kSmallCastElems elements:
+// amax, scale and cast in one single-workgroup launch; writes *amax_out and *scale_out.
+constexpr int64_t kSmallCastElems = 16384;
+int launch_cast_small_current(const CastArgs& a, hipStream_t st);
+
 struct GemmArgs {
     int mode, afmt, bfmt;
     // BLOCK / BLOCK_E8M0 only: a_static = the activation operand has one per-tensor scale, *Aglobal

@@ -574,6 +574,53 @@ __global__ __launch_bounds__(256) void cast_generic_kernel(CastArgs a, int br, i
     if (FUSED_AMAX && threadIdx.x == 0) atomicMax(reinterpret_cast<uint32_t*>(a.amax_out), bm);
 }
 
+// ------------------------------------------------------------------ small tensors, current scaling
+// Per-tensor current scaling of a tensor of at most kSmallElems elements in one workgroup: the
+// amax, the scale fl(amax / MAX) and the cast in one launch instead of three (zero, amax, cast),
+// which is what such a tensor's time consists of.  IEEE division and the exact encoder, as in the
+// generic kernel; either output layout, or both (dual cast, q2 set).
+template <int FMT, bool BF16>
+__global__ __launch_bounds__(1024) void cast_small_current_kernel(CastArgs a) {
+    const int64_t n = a.rows * a.cols;
+    auto load = [&](int64_t i) -> float {
+        const int64_t r = i / a.cols, c = i - r * a.cols;
+        if (BF16) return bf16lo(static_cast<const uint16_t*>(a.x)[r * a.ld + c]);
+        return static_cast<const float*>(a.x)[r * a.ld + c];
+    };
+    uint32_t m = 0;
+    for (int64_t i = threadIdx.x; i < n; i += 1024) m = max(m, absbits(load(i)));
+    __shared__ uint32_t red[16];
+    m = wave_max_u32(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    uint32_t bm = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) bm = max(bm, red[w]);
+    const float s = scale_from_amax<FMT>(__uint_as_float(bm), 1.0f);
+    if (threadIdx.x == 0) {
+        reinterpret_cast<uint32_t*>(a.amax_out)[0] = bm;
+        *a.scale_out = s;
+    }
+    for (int64_t i = threadIdx.x; i < n; i += 1024) {
+        const int64_t r = i / a.cols, c = i - r * a.cols;
+        const uint8_t code = (uint8_t)code_slow<FMT>(load(i) / s);
+        if (a.transpose) a.q[c * a.ldq + r] = code;
+        else a.q[r * a.ldq + c] = code;
+        if (a.q2) a.q2[r * a.ldq2 + c] = code;     // dual cast: the row-layout copy as well
+    }
+}
+
+int launch_cast_small_current(const CastArgs& a, hipStream_t st) {
+    if (a.fmt == kE4M3) {
+        if (a.bf16) hipLaunchKernelGGL((cast_small_current_kernel<kE4M3, true>), dim3(1), dim3(1024), 0, st, a);
+        else hipLaunchKernelGGL((cast_small_current_kernel<kE4M3, false>), dim3(1), dim3(1024), 0, st, a);
+    } else {
+        if (a.bf16) hipLaunchKernelGGL((cast_small_current_kernel<kE5M2, true>), dim3(1), dim3(1024), 0, st, a);
+        else hipLaunchKernelGGL((cast_small_current_kernel<kE5M2, false>), dim3(1), dim3(1024), 0, st, a);
+    }
+    return 0;
+}
+
 // ------------------------------------------------------------------ dispatch
 template <int FMT, int MODE, bool BF16, bool FUSED, bool DERIVE>
 static void dispatch_shape(const CastArgs& a, hipStream_t st) {
