@@ -482,20 +482,27 @@ __global__ __launch_bounds__(kTileThreads) void cast_dual_run_kernel(CastArgs a)
 }
 
 // ------------------------------------------------------------------ 128x128 weight blocks
-// One workgroup per 128x128 block (non-transposed, rows % 128 == 0, cols % 128 == 0): thread t
-// holds row t/2, columns (t%2)*64 .. +64 in registers; block amax via LDS; one pass over HBM.
+// One workgroup per 128x128 block (non-transposed, rows % 128 == 0, cols % 128 == 0), the block in
+// registers; block amax via LDS; one pass over HBM.  Sixteen consecutive lanes cover one row's 128
+// values (8 each), so every load and store instruction reads or writes whole row segments; thread
+// t holds columns 8 (t % 16) .. +8 of rows t / 16 + 16 j, j = 0 .. 7.
 template <int FMT, bool BF16, bool E8>
 __global__ __launch_bounds__(256) void cast_block128_kernel(CastArgs a) {
     const int64_t br = blockIdx.y, bc = blockIdx.x;
     const int t = threadIdx.x;
-    const int64_t r = br * 128 + (t >> 1), c = bc * 128 + (t & 1) * 64;
+    const int64_t r0 = br * 128 + (t >> 4), c = bc * 128 + (t & 15) * 8;
     const size_t esz = BF16 ? 2 : 4;
-    const char* src = static_cast<const char*>(a.x) + (r * a.ld + c) * esz;
+    const char* src = static_cast<const char*>(a.x) + (r0 * a.ld + c) * esz;
     float v[64];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) load8<BF16>(src + j * 8 * esz, v + 8 * j);
-    const uint32_t m0 = chunk_max<32>(v), m1 = chunk_max<32>(v + 32);
-    uint32_t m = wave_max_u32(max(m0, m1));
+    for (int j = 0; j < 8; ++j) load8<BF16>(src + (int64_t)j * 16 * a.ld * esz, v + 8 * j);
+    uint32_t mj[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mj[j] = chunk_max<8>(v + 8 * j);
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = max(m, mj[j]);
+    m = wave_max_u32(m);
     __shared__ uint32_t red[4];
     if ((t & 63) == 0) red[t >> 6] = m;
     __syncthreads();
@@ -504,19 +511,21 @@ __global__ __launch_bounds__(256) void cast_block128_kernel(CastArgs a) {
     if constexpr (E8) {
         // power-of-two block scale: the MX exponent rule over the whole block, exact scaling
         const int e = mx_exponent<FMT>(__uint_as_float(bm));
-        cast_mx<FMT, 32>(v, -e, m0 > 0x7F800000u, out);
-        cast_mx<FMT, 32>(v + 32, -e, m1 > 0x7F800000u, out + 8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cast_mx<FMT, 8>(v + 8 * j, -e, mj[j] > 0x7F800000u, out + 2 * j);
         if (t == 0) reinterpret_cast<uint8_t*>(a.scales)[br * (a.cols / 128) + bc] = (uint8_t)(e + 127);
     } else {
         const float s = scale_from_amax<FMT>(__uint_as_float(bm), 1.0f);
         const float y = recip_rn(s);
-        cast_div<FMT, false, 32>(v, s, y, 0, divisor_ok(s) && dividends_ok(m0, chunk_min_m1<32>(v)), out);
-        cast_div<FMT, false, 32>(v + 32, s, y, 0, divisor_ok(s) && dividends_ok(m1, chunk_min_m1<32>(v + 32)), out + 8);
+        const bool sok = divisor_ok(s);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            cast_div<FMT, false, 8>(v + 8 * j, s, y, 0, sok && dividends_ok(mj[j], chunk_min_m1<8>(v + 8 * j)), out + 2 * j);
         if (t == 0) reinterpret_cast<float*>(a.scales)[br * (a.cols / 128) + bc] = s;
     }
-    uint8_t* dst = a.q + r * a.ldq + c;
-    store32(dst, out);
-    store32(dst + 32, out + 8);
+    uint8_t* dst = a.q + r0 * a.ldq + c;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<uint2*>(dst + (int64_t)j * 16 * a.ldq) = make_uint2(out[2 * j], out[2 * j + 1]);
 }
 
 // ------------------------------------------------------------------ generic exact fallback
