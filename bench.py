@@ -16,7 +16,12 @@ dequantization, and the block GEMM with UE8M0 weight scales and with a static ac
 The headline value is the step's total GEMM flops (2 M N K per GEMM) divided by the step time,
 i.e. scaled-GEMM TFLOP/s including every quantization the path performs.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+The timed steps are replays of HIP graphs captured from the same library calls (one graph per
+delayed-scaling step index, since that input changes with the step); --no-graph times eager
+launches instead.  Per-kernel times and the roofline come from a second pass of K eager steps with
+HIP events around each launch, whose step time is reported as ms_per_step_eager.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-graph]
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -43,6 +48,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the steps as eager launches instead of HIP graph replays")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run one plain 256 MiB device copy (read + write) whose "
                          "known size calibrates the HBM byte counters of a profiler run")
@@ -222,16 +229,39 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+
+    def timed_steps(run):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(args.steps):
+            run(args.warmup + i)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / args.steps
+
+    graph_ms = None
+    if not args.no_graph:
+        # One graph per delayed-scaling input index (the step's only varying argument); the library
+        # launches on torch's current stream, which is the capture stream inside the block.  Replays
+        # advance the delayed-scaling state exactly as eager steps do.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graphs = []
+        for t in range(16):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                step(t)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % 16].replay()
+        graph_ms = timed_steps(lambda i: graphs[i % 16].replay())
+    # eager steps with per-launch events: the per-kernel times and the roofline
     timer.enabled = True
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    end.record()
-    torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / args.steps
+    eager_ms = timed_steps(step)
+    ms_per_step = graph_ms if graph_ms is not None else eager_ms
     tflops = step_flops / (ms_per_step * 1e-3) / 1e12
 
     per = {}
@@ -270,7 +300,9 @@ def main():
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8 e4m3/e5m2 operands, fp32 accumulate", "data": "synthetic (seeded numpy PCG64)",
-        "config": {"workload": WORKLOAD, "gemm_tflop_per_step": round(step_flops / 1e12, 4), "parallelism": "single GPU"},
+        "config": {"workload": WORKLOAD, "gemm_tflop_per_step": round(step_flops / 1e12, 4), "parallelism": "single GPU",
+                   "launch": "eager" if graph_ms is None else "HIP graph replay, one graph per delayed-scaling step"},
+        "ms_per_step_eager": round(eager_ms, 4),
         "pct_fp8_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
         "quantize_gbs": round(quant_gbs, 1), "quantize_pct_hbm_peak": round(100 * quant_gbs / PEAK_HBM_GBS, 2),
         "roofline": roofline, "per_kernel": per, "next_rows": next_rows, "input_gen_s": round(gen_s, 1),
