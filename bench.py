@@ -394,7 +394,7 @@ def cpu_baseline(h):
     qb, sb = orc.quantize_tensor_current(h["b1"], 0, transpose=True)
     orc.gemm_ref(orc.dequantize(0, qa, 0, None, sa), orc.dequantize(0, qb, 0, None, sb))
     flops += 2 * 16 * 64 * 32
-    r = 2048  # sampled rows of each operand for the large workloads
+    r = 3072  # sampled rows of each operand for the large workloads
     # fine-grained: r rows of X and one 128-row block of W, GEMM r x 128 x 7168
     qx, sx = orc.quantize_block(np.ascontiguousarray(h["X3"][:r]), 0, 1, 128)
     qw, sw = orc.quantize_block(np.ascontiguousarray(h["W3"][:128]), 0, 128, 128)
@@ -421,7 +421,7 @@ def cpu_baseline(h):
     secs = time.time() - t0
     return {"value": round(flops / secs / 1e12, 8), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "seconds": round(secs, 2),
-            "sample": ("oracle quantize + fp64 GEMM: whole per-tensor workload; 2048-row samples of the fine-grained "
+            "sample": ("oracle quantize + fp64 GEMM: whole per-tensor workload; 3072-row samples of the fine-grained "
                        "(x one 128-row weight block), MX and all six MOSS copies (global factors over whole "
                        "tensors), GEMMs over those rows/columns; delayed workload not sampled")}
 
