@@ -13,6 +13,7 @@ After the timed steps, the next-step paths are timed on the same inputs (reporte
 "next_rows", not part of the headline): automatic weight scaling against a just-in-time max
 reduction of W, the delayed-scaling history merge, UE8M0 128x128 weight quantization and block
 dequantization, and the block GEMM with UE8M0 weight scales and with a static activation scale.
+Each cast is also timed alone, cold (input from HBM) and warm ("quantize_cold_warm").
 The headline value is the step's total GEMM flops (2 M N K per GEMM) divided by the step time,
 i.e. scaled-GEMM TFLOP/s including every quantization the path performs.
 
@@ -288,6 +289,7 @@ def main():
                 "traffic": measured_traffic() if dom == "g5" else None, "traffic_unit": "bytes per launch",
                 "avg_launch_ms": round(dom_ms, 5)}
     next_rows = measure_next(torch, fq, o, w3, w5, args.steps)
+    cold_warm = measure_casts_cold_warm(torch, fq, o, w2, w3, w4, w5)
     if args.copy_calibration:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -305,11 +307,66 @@ def main():
         "ms_per_step_eager": round(eager_ms, 4),
         "pct_fp8_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
         "quantize_gbs": round(quant_gbs, 1), "quantize_pct_hbm_peak": round(100 * quant_gbs / PEAK_HBM_GBS, 2),
-        "roofline": roofline, "per_kernel": per, "next_rows": next_rows, "input_gen_s": round(gen_s, 1),
+        "roofline": roofline, "per_kernel": per, "quantize_cold_warm": cold_warm, "next_rows": next_rows,
+        "input_gen_s": round(gen_s, 1),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(host_inputs)
     print(json.dumps(out), flush=True)
+
+
+def measure_casts_cold_warm(torch, fq, o, w2, w3, w4, w5, reps=10):
+    """Each cast of the step timed alone (HIP events around it), cold and warm.  Cold: before every
+    launch a 1 GiB buffer is read, which leaves only clean, unrelated lines in L2 and the 256 MB
+    last-level cache, so the input comes from HBM and no earlier writes are pending.  Warm: the
+    same launch repeated back to back, so an input that fits the last-level cache is served from
+    it.  GB/s counts the algorithmic bytes (input read, plus the amax pass's read where the scale
+    is derived, FP8 and scale bytes written)."""
+    dev = "cuda:0"
+    E4M3, E5M2 = fq.E4M3, fq.E5M2
+    TENSOR, BLOCK, MX, MOSS = fq.TENSOR, fq.BLOCK, fq.MX, fq.MOSS
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    Q, QD = fq.fp8_quantize, fq.fp8_quantize_dual
+    casts = {
+        "delayed A 1024x2048 (fused amax)": (lambda: Q(TENSOR, E4M3, w2["A"][0], o["q2a"], None, o["s2a"], True, o["m2a"]),
+                                             1024 * 2048 * 3),
+        "1x128 X 4096x7168": (lambda: Q(BLOCK, E4M3, w3["X"], o["q3x"], o["s3x"], block=(1, 128)),
+                              4096 * 7168 * 3 + 4096 * 56 * 4),
+        "128x128 W 2048x7168": (lambda: Q(BLOCK, E4M3, w3["W"], o["q3w"], o["s3w"], block=(128, 128)),
+                                2048 * 7168 * 3 + 16 * 56 * 4),
+        "MX A 8192x8192": (lambda: Q(MX, E4M3, w4["A"], o["q4a"], o["e4a"]), 8192 * 8192 * 3 + 8192 * 256),
+        "MOSS X 16384x4096 (amax + dual cast)": (
+            lambda: QD(MOSS, E4M3, w5["X"], o["q5X"], o["e5X"], o["q5XT"], o["e5XT"], o["S5X"], False, o["m5X"]),
+            16384 * 4096 * 6 + 2 * 16384 * 128),
+    }
+    out = {}
+    for name, (fn, nbytes) in casts.items():
+        fn()
+        torch.cuda.synchronize()
+        cold = []
+        for _ in range(reps):
+            torch.sum(flush, dim=0, keepdim=True, out=sink)
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            cold.append((s, e))
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        cold_ms = sorted(a.elapsed_time(b) for a, b in cold)[reps // 2]
+        warm_ms = s.elapsed_time(e) / reps
+        out[name] = {"cold_ms": round(cold_ms, 5), "cold_gbs": round(nbytes / (cold_ms * 1e-3) / 1e9, 1),
+                     "cold_pct_hbm_peak": round(100 * nbytes / (cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                     "warm_ms": round(warm_ms, 5), "warm_gbs": round(nbytes / (warm_ms * 1e-3) / 1e9, 1)}
+    del flush
+    return out
 
 
 def measure_next(torch, fq, o, w3, w5, reps):
