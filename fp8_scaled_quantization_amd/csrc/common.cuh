@@ -37,6 +37,18 @@ __device__ __forceinline__ void load8(const void* p, float* v) {
 
 __device__ __forceinline__ uint32_t absbits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
 
+// max |x| of the 2N bf16 values packed two per word in w, as the fp32 bits of that magnitude:
+// magnitudes of bf16 (and NaN above Inf) order like their 15-bit patterns, so one packed 16-bit
+// max per word replaces an unpack, a mask and a max per value
+template <int N>
+__device__ __forceinline__ uint32_t bf16w_absmax(const uint32_t* w) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    u16x2 m = {0, 0};
+#pragma unroll
+    for (int j = 0; j < N; ++j) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[j] & 0x7FFF7FFFu));
+    return (uint32_t)max(m[0], m[1]) << 16;
+}
+
 // ------------------------------------------------------------------ FP8 packing
 // Four fp32 -> four FP8 bytes, byte i = code(v_i).  Inputs must already be clipped to +-MAX.
 template <int FMT>

@@ -389,6 +389,7 @@ __global__ __launch_bounds__(kTileThreads) void cast_transposed_kernel(CastArgs 
 // are completed inside one L2.
 template <int FMT, int MODE, bool FUSED_AMAX, bool DERIVE, int NB>
 __global__ __launch_bounds__(kTileThreads) void cast_dual_run_kernel(CastArgs a) {
+    static_assert(MODE == kModeTensor || MODE == kModeMX || MODE == kModeMoss, "dual casts: TENSOR, MX, MOSS");
     constexpr int TC = kTileCols, NT = kTileThreads;
     __shared__ __attribute__((aligned(16))) uint32_t tile[2][TC * 64];
     __shared__ __attribute__((aligned(16))) uint8_t tsc[TC][4 * NB];
@@ -435,8 +436,9 @@ __global__ __launch_bounds__(kTileThreads) void cast_dual_run_kernel(CastArgs a)
             float v[32];
 #pragma unroll
             for (int q = 0; q < 16; ++q) { v[2 * q] = bf16lo(wv[q]); v[2 * q + 1] = bf16hi(wv[q]); }
-            uint32_t out[8], sc = 0, cm = 0;
-            process_chunk<FMT, MODE, true, 8>(v, u, out, sc, cm);
+            uint32_t out[8], sc = 0;
+            const uint32_t cm = bf16w_absmax<16>(wv);
+            cast_group<FMT, MODE, true, 32>(v, cm, cm, u, out, sc);
             const int64_t r = band * 128 + rr;
             uint8_t* dst = a.q2 + r * a.ldq2 + c0 + 32 * h;
             *reinterpret_cast<uint4*>(dst + 16 * odd) = make_uint4(out[0], out[1], out[2], out[3]);
@@ -449,18 +451,20 @@ __global__ __launch_bounds__(kTileThreads) void cast_dual_run_kernel(CastArgs a)
         __syncthreads();
         {
             float v[32];
+            uint32_t pw[16];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint4 q4 = *reinterpret_cast<const uint4*>(&tl[pair_word(oc, seg * 16 + 4 * i)]);
-                const uint32_t ww[4] = {q4.x, q4.y, q4.z, q4.w};
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    v[8 * i + 2 * d] = bf16lo(ww[d]);
-                    v[8 * i + 2 * d + 1] = bf16hi(ww[d]);
-                }
+                pw[4 * i] = q4.x;
+                pw[4 * i + 1] = q4.y;
+                pw[4 * i + 2] = q4.z;
+                pw[4 * i + 3] = q4.w;
             }
-            uint32_t out[8], sc = 0, cm = 0;
-            process_chunk<FMT, MODE, true, 8>(v, u, out, sc, cm);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) { v[2 * q] = bf16lo(pw[q]); v[2 * q + 1] = bf16hi(pw[q]); }
+            uint32_t out[8], sc = 0;
+            const uint32_t cm = bf16w_absmax<16>(pw);
+            cast_group<FMT, MODE, true, 32>(v, cm, cm, u, out, sc);
             store32(a.q + (c0 + oc) * a.ldq + band * 128 + seg * 32, out);
             if (MODE == kModeMX || MODE == kModeMoss) tsc[oc][4 * (band - b0) + seg] = (uint8_t)sc;
         }
