@@ -133,20 +133,24 @@ __device__ __forceinline__ void copy8(uint8_t* lds, rsrc_t rs, uint32_t voff0, u
     dma16(lds_addr(lds), rs, voff, koff);
 }
 
-// Group 0, wave wi: A rows 64 wi .. +64 of step s (8 copies).
-__device__ __forceinline__ void copy_A(uint8_t* smem, int s, int wi, rsrc_t ra, uint32_t voffA, uint32_t lda) {
+// Wave wi: A rows 64 wi .. +64 of step ks into the stage of step s (8 copies).  ks = s except past
+// the last step, where the copies repeat the last step's data into a stage no step reads, so that
+// the main loop has no branches and the same wait counts in every iteration.
+__device__ __forceinline__ void copy_A(uint8_t* smem, int s, int ks, int wi, rsrc_t ra, uint32_t voffA, uint32_t lda) {
     uint8_t* st = smem + (s & 1) * kStage;
-    const uint32_t koff = (uint32_t)s * BK;
+    const uint32_t koff = (uint32_t)ks * BK;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const uint32_t r0 = (uint32_t)(wi * 64 + j * 8);
         copy8(st + r0 * BK, ra, voffA, r0 * lda, koff);
     }
 }
-// Group 1, wave wi: B rows base + 32 wi .. +32 of step s (4 copies); base 0 (B0) or 128 (B1).
-__device__ __forceinline__ void copy_B(uint8_t* smem, int s, int base, int wi, rsrc_t rb, uint32_t voffB, uint32_t ldb) {
+// Wave wi: B rows base + 32 wi .. +32 of step ks into the stage of step s (4 copies); base 0 (B0)
+// or 128 (B1).
+__device__ __forceinline__ void copy_B(uint8_t* smem, int s, int ks, int base, int wi, rsrc_t rb, uint32_t voffB,
+                                       uint32_t ldb) {
     uint8_t* st = smem + (s & 1) * kStage + kA;
-    const uint32_t koff = (uint32_t)s * BK;
+    const uint32_t koff = (uint32_t)ks * BK;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const uint32_t r0 = (uint32_t)(base + wi * 32 + j * 8);
@@ -230,22 +234,20 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // ---- prologue: group 1 sends all of step 0 but B1, plus A and B0 of step 1; group 0 sends B1
-    // of step 0 (it sends B1 of step k+1 in its memory phase for step k)
+    // ---- prologue: group 1 sends A and B0 of step 0 and A of step 1; group 0 sends B1 of step 0
+    // and B0 of step 1 (afterwards it sends B1 of step k+1 in its memory phase for step k and B0
+    // of step k+2 after its MFMAs for step k; group 1 sends A of step k+2 in its memory phase)
+    const int k1 = nk > 1 ? 1 : 0;
     if (grp == 0) {
-        copy_B(smem, 0, 128, wi, rb, voffB, uldb);
-        wait_vm0();
+        copy_B(smem, 0, 0, 128, wi, rb, voffB, uldb);
+        copy_B(smem, 1, k1, 0, wi, rb, voffB, uldb);
+        wait_vm<4>();
     } else {
-        copy_A(smem, 0, wi, ra, voffA, ulda);
-        copy_B(smem, 0, 0, wi, rb, voffB, uldb);
+        copy_A(smem, 0, 0, wi, ra, voffA, ulda);
+        copy_B(smem, 0, 0, 0, wi, rb, voffB, uldb);
         if (SCALED) copy_quad(smem, 0, wi, rsa, rsb, voffS, usc);
-        if (nk > 1) {
-            copy_A(smem, 1, wi, ra, voffA, ulda);
-            copy_B(smem, 1, 0, wi, rb, voffB, uldb);
-            wait_vm<12>();
-        } else {
-            wait_vm0();
-        }
+        copy_A(smem, 1, k1, wi, ra, voffA, ulda);
+        wait_vm<8>();
     }
     barrier();
     v8i fa[4], fb[8];
@@ -274,12 +276,11 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
             const uint8_t* sb = sa + kA;
             if (grp == 0) {
                 // A and B0 of step k; B1 of step k+1 (4 copies), one per three fragment reads
-                const bool cp = k + 1 < nk;
                 uint8_t* st = smem + ((k + 1) & 1) * kStage + kA;
-                const uint32_t koff = (uint32_t)(k + 1) * BK;
+                const uint32_t koff = (uint32_t)min(k + 1, nk - 1) * BK;
 #pragma unroll
                 for (int q = 0; q < 12; ++q) {
-                    if (cp && q % 3 == 0) {
+                    if (q % 3 == 0) {
                         const uint32_t r0 = (uint32_t)(128 + wi * 32 + (q / 3) * 8);
                         copy8(st + r0 * BK, rb, voffB, r0 * uldb, koff);
                     }
@@ -287,30 +288,25 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
                     else fb[q - 4] = frag(sb + rowB + (q - 4) * 16 * BK, cLo, cHi);
                 }
                 // B1 of step k (sent one memory phase ago) lands before group 1 reads it next phase;
-                // newer: B0 of step k+1 (sent in the last compute phase) and this phase's B1
-                if (cp && k >= 1) wait_vm<8>();
-                else if (cp) wait_vm<4>();
-                else wait_vm0();
+                // newer: B0 of step k+1 (sent in the last compute phase, or the prologue) and this
+                // phase's B1
+                wait_vm<8>();
             } else {
                 // B1 of step k; A of step k+2 (8 copies, one per fragment read) and the scale quad
-                const bool cp = k + 2 < nk;
                 uint8_t* st = smem + (k & 1) * kStage;
-                const uint32_t koff = (uint32_t)(k + 2) * BK;
+                const uint32_t koff = (uint32_t)min(k + 2, nk - 1) * BK;
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
-                    if (cp) {
-                        const uint32_t r0 = (uint32_t)(wi * 64 + q * 8);
-                        copy8(st + r0 * BK, ra, voffA, r0 * ulda, koff);
-                    }
+                    const uint32_t r0 = (uint32_t)(wi * 64 + q * 8);
+                    copy8(st + r0 * BK, ra, voffA, r0 * ulda, koff);
                     fb[q] = frag(sb + rowB + q * 16 * BK, cLo, cHi);
                 }
-                const bool quad = SCALED && cp && ((k + 2) & 3) == 0;
+                const bool quad = SCALED && k + 2 < nk && ((k + 2) & 3) == 0;
                 if (quad) copy_quad(smem, k + 2, wi, rsa, rsb, voffS, usc);
-                // A of step k+1 (sent one memory phase ago) lands before group 0 reads it next
-                // phase; this phase's copies may stay in flight
+                // A of step k+1 (sent one memory phase ago, or in the prologue) lands before group 0
+                // reads it next phase; this phase's copies may stay in flight
                 if (quad) wait_vm<10>();
-                else if (cp) wait_vm<8>();
-                else wait_vm0();
+                else wait_vm<8>();
             }
         }
         if (SCALED) {
@@ -332,8 +328,9 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
         }
         wait_lgkm0();
         barrier();
-        // ---- compute phase (group 1 also reads A of step k+1, row block by row block)
-        const bool next_a = grp == 1 && k + 1 < nk;
+        // ---- compute phase (group 1 also reads A of step k+1, row block by row block; past the
+        // last step it reads a stage it does not use)
+        const bool next_a = grp == 1;
         const uint8_t* sn = smem + ((k + 1) & 1) * kStage;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -360,24 +357,21 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
         if (grp == 0) {
             // B0 of step k+2, into the stage group 0 finished reading last phase, sent after this
             // phase's MFMAs: group 1's memory phase, which moves A, is the longer one
-            if (k + 2 < nk) {
-                uint8_t* st = smem + (k & 1) * kStage + kA;
-                const uint32_t koff = (uint32_t)(k + 2) * BK;
+            uint8_t* st = smem + (k & 1) * kStage + kA;
+            const uint32_t koff = (uint32_t)min(k + 2, nk - 1) * BK;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t r0 = (uint32_t)(wi * 32 + j * 8);
-                    copy8(st + r0 * BK, rb, voffB, r0 * uldb, koff);
-                }
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t r0 = (uint32_t)(wi * 32 + j * 8);
+                copy8(st + r0 * BK, rb, voffB, r0 * uldb, koff);
             }
-            // B0 of step k+1 (sent in the last compute phase) lands before group 0 reads it next
-            // phase; newer: B1 of step k+1 (this memory phase) and B0 of step k+2
-            if (k + 2 < nk) wait_vm<8>();
-            else if (k + 1 < nk) wait_vm<4>();
-            else wait_vm0();
+            // B0 of step k+1 (sent in the last compute phase, or the prologue) lands before group 0
+            // reads it next phase; newer: B1 of step k+1 (this memory phase) and B0 of step k+2
+            wait_vm<8>();
         }
         barrier();
     }
     if (grp == 0) barrier();          // matches group 1's extra barrier at the start
+    wait_vm0();                       // the last steps' repeated copies
 
     // ---- epilogue
     const float f = (MODE == kModeTensor || MODE == kModeMoss) ? ga * gb : 1.0f;

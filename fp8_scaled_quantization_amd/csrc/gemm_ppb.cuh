@@ -52,10 +52,13 @@ constexpr size_t lds_bytes() { return (size_t)kScBase + 2 * (size_t)quad_rows<MO
 
 // This wave's half of step s: group g, wave wi sends A rows 128 g + 32 wi .. +32 (4 copies) and
 // B rows 64 g + 16 wi .. +16 (2 copies).  j selects one of the six.
-__device__ __forceinline__ void copy_one(uint8_t* smem, int s, int g, int wi, int j, rsrc_t ra, rsrc_t rb,
+// The data of step ks goes into the stage of step s (ks = s except past the last step, where the
+// copies repeat the last step's data into a stage no step reads, which keeps the loop free of
+// branches).
+__device__ __forceinline__ void copy_one(uint8_t* smem, int s, int ks, int g, int wi, int j, rsrc_t ra, rsrc_t rb,
                                          uint32_t voffA, uint32_t voffB, uint32_t lda, uint32_t ldb) {
     uint8_t* st = smem + (s % STAGES) * kStage;
-    const uint32_t koff = (uint32_t)s * BK;
+    const uint32_t koff = (uint32_t)ks * BK;
     if (j < 4) {
         const uint32_t r0 = (uint32_t)(128 * g + 32 * wi + 8 * j);
         copy8(st + r0 * BK, ra, voffA, r0 * lda, koff);
@@ -174,11 +177,11 @@ __global__ __launch_bounds__(512, 1) void gemm_ppb_kernel(GemmArgs g) {
 
     // ---- prologue: both halves of steps 0 and 1, the first scale quad
 #pragma unroll
-    for (int j = 0; j < 6; ++j) copy_one(smem, 0, grp, wi, j, ra, rb, voffA, voffB, ulda, uldb);
+    for (int j = 0; j < 6; ++j) copy_one(smem, 0, 0, grp, wi, j, ra, rb, voffA, voffB, ulda, uldb);
     if (!(BLOCKED && AST)) issue_quad<MODE>(smem, 0, grp, wi, rsa, rsb, voffS, sc_row);
     if (nk > 1) {
 #pragma unroll
-        for (int j = 0; j < 6; ++j) copy_one(smem, 1, grp, wi, j, ra, rb, voffA, voffB, ulda, uldb);
+        for (int j = 0; j < 6; ++j) copy_one(smem, 1, 1, grp, wi, j, ra, rb, voffA, voffB, ulda, uldb);
         wait_vm<6>();
     } else {
         wait_vm0();
@@ -218,7 +221,7 @@ __global__ __launch_bounds__(512, 1) void gemm_ppb_kernel(GemmArgs g) {
         v8i fa[4], fb[4];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            if (cp && q < 6) copy_one(smem, k + 2, grp, wi, q, ra, rb, voffA, voffB, ulda, uldb);
+            if (q < 6) copy_one(smem, k + 2, min(k + 2, nk - 1), grp, wi, q, ra, rb, voffA, voffB, ulda, uldb);
             if (q < 4) fa[q] = frag(sa + rowA + q * 16 * BK, cLo, cHi);
             else fb[q - 4] = frag(sb + rowB + (q - 4) * 16 * BK, cLo, cHi);
         }
@@ -246,8 +249,7 @@ __global__ __launch_bounds__(512, 1) void gemm_ppb_kernel(GemmArgs g) {
         // this wave's copies of step k+1 (sent one memory phase ago) land before the barrier; the
         // ones sent in this phase may stay in flight
         if (quad) wait_vm<7>();
-        else if (cp) wait_vm<6>();
-        else wait_vm0();
+        else wait_vm<6>();
         wait_lgkm0();
         barrier();
         // the next step's weight-scale word: nothing in the compute phase waits on it
@@ -298,6 +300,7 @@ __global__ __launch_bounds__(512, 1) void gemm_ppb_kernel(GemmArgs g) {
         barrier();
     }
     if (grp == 0) barrier();          // matches group 1's extra barrier at the start
+    wait_vm0();                       // the last steps' repeated copies
 
     // ---- epilogue
     const float f = (MODE == kModeTensor || MODE == kModeMoss) ? ga * gb : 1.0f;
