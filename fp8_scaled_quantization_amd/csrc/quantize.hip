@@ -489,47 +489,52 @@ __global__ __launch_bounds__(kTileThreads) void cast_dual_run_kernel(CastArgs a)
 // One workgroup per 128x128 block (non-transposed, rows % 128 == 0, cols % 128 == 0), the block in
 // registers; block amax via LDS; one pass over HBM.  Sixteen consecutive lanes cover one row's 128
 // values (8 each), so every load and store instruction reads or writes whole row segments; thread
-// t holds columns 8 (t % 16) .. +8 of rows t / 16 + 16 j, j = 0 .. 7.
-template <int FMT, bool BF16, bool E8>
-__global__ __launch_bounds__(256) void cast_block128_kernel(CastArgs a) {
+// t holds columns 8 (t % 16) .. +8 of rows t / 16 + (NT / 16) j, j < 2048 / NT.
+template <int FMT, bool BF16, bool E8, int NT = 512>
+__global__ __launch_bounds__(NT) void cast_block128_kernel(CastArgs a) {
+    constexpr int RPT = 128 * 16 / NT;            // rows per thread, NT / 16 rows apart
+    constexpr int NW = NT / 64;
     const int64_t br = blockIdx.y, bc = blockIdx.x;
     const int t = threadIdx.x;
     const int64_t r0 = br * 128 + (t >> 4), c = bc * 128 + (t & 15) * 8;
     const size_t esz = BF16 ? 2 : 4;
     const char* src = static_cast<const char*>(a.x) + (r0 * a.ld + c) * esz;
-    float v[64];
+    float v[8 * RPT];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) load8<BF16>(src + (int64_t)j * 16 * a.ld * esz, v + 8 * j);
-    uint32_t mj[8];
+    for (int j = 0; j < RPT; ++j) load8<BF16>(src + (int64_t)j * (NT / 16) * a.ld * esz, v + 8 * j);
+    uint32_t mj[RPT];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) mj[j] = chunk_max<8>(v + 8 * j);
+    for (int j = 0; j < RPT; ++j) mj[j] = chunk_max<8>(v + 8 * j);
     uint32_t m = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m = max(m, mj[j]);
+    for (int j = 0; j < RPT; ++j) m = max(m, mj[j]);
     m = wave_max_u32(m);
-    __shared__ uint32_t red[4];
+    __shared__ uint32_t red[NW];
     if ((t & 63) == 0) red[t >> 6] = m;
     __syncthreads();
-    const uint32_t bm = max(max(red[0], red[1]), max(red[2], red[3]));
-    uint32_t out[16];
+    uint32_t bm = red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) bm = max(bm, red[w]);
+    uint32_t out[2 * RPT];
     if constexpr (E8) {
         // power-of-two block scale: the MX exponent rule over the whole block, exact scaling
         const int e = mx_exponent<FMT>(__uint_as_float(bm));
 #pragma unroll
-        for (int j = 0; j < 8; ++j) cast_mx<FMT, 8>(v + 8 * j, -e, mj[j] > 0x7F800000u, out + 2 * j);
+        for (int j = 0; j < RPT; ++j) cast_mx<FMT, 8>(v + 8 * j, -e, mj[j] > 0x7F800000u, out + 2 * j);
         if (t == 0) reinterpret_cast<uint8_t*>(a.scales)[br * (a.cols / 128) + bc] = (uint8_t)(e + 127);
     } else {
         const float s = scale_from_amax<FMT>(__uint_as_float(bm), 1.0f);
         const float y = recip_rn(s);
         const bool sok = divisor_ok(s);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < RPT; ++j)
             cast_div<FMT, false, 8>(v + 8 * j, s, y, 0, sok && dividends_ok(mj[j], chunk_min_m1<8>(v + 8 * j)), out + 2 * j);
         if (t == 0) reinterpret_cast<float*>(a.scales)[br * (a.cols / 128) + bc] = s;
     }
     uint8_t* dst = a.q + r0 * a.ldq + c;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<uint2*>(dst + (int64_t)j * 16 * a.ldq) = make_uint2(out[2 * j], out[2 * j + 1]);
+    for (int j = 0; j < RPT; ++j)
+        *reinterpret_cast<uint2*>(dst + (int64_t)j * (NT / 16) * a.ldq) = make_uint2(out[2 * j], out[2 * j + 1]);
 }
 
 // ------------------------------------------------------------------ generic exact fallback
@@ -650,8 +655,8 @@ static void dispatch_shape(const CastArgs& a, hipStream_t st) {
     }
     const bool block128 = (MODE == kModeBlock || MODE == kModeBlockE8) && a.block_r == 128 && a.block_c == 128;
     if (!a.transpose && block128 && !FUSED && a.rows % 128 == 0 && a.cols % 128 == 0) {
-        hipLaunchKernelGGL((cast_block128_kernel<FMT, BF16, MODE == kModeBlockE8>),
-                           dim3((unsigned)(a.cols / 128), (unsigned)(a.rows / 128)), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((cast_block128_kernel<FMT, BF16, MODE == kModeBlockE8, 512>),
+                           dim3((unsigned)(a.cols / 128), (unsigned)(a.rows / 128)), dim3(512), 0, st, a);
         return;
     }
     if constexpr (MODE == kModeBlockE8) {
