@@ -48,6 +48,18 @@ __device__ __forceinline__ uint32_t bf16w_absmax(const uint32_t* w) {
     for (int j = 0; j < N; ++j) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[j] & 0x7FFF7FFFu));
     return (uint32_t)max(m[0], m[1]) << 16;
 }
+// min over the same values of (|x| bits - 1) as fp32 bits, a zero wrapping to 0xFFFFFFFF: per
+// 16-bit half (|x| - 1) wraps the same way, and (d << 16) | 0xFFFF maps it monotonically onto the
+// fp32 difference, so the packed min gives the exact value
+template <int N>
+__device__ __forceinline__ uint32_t bf16w_minm1(const uint32_t* w) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    const u16x2 one = {1, 1};
+    u16x2 m = {0xFFFF, 0xFFFF};
+#pragma unroll
+    for (int j = 0; j < N; ++j) m = __builtin_elementwise_min(m, __builtin_bit_cast(u16x2, w[j] & 0x7FFF7FFFu) - one);
+    return ((uint32_t)min(m[0], m[1]) << 16) | 0xFFFFu;
+}
 
 // ------------------------------------------------------------------ FP8 packing
 // Four fp32 -> four FP8 bytes, byte i = code(v_i).  Inputs must already be clipped to +-MAX.

@@ -166,11 +166,11 @@ __device__ __forceinline__ void cast_group(const float* v, uint32_t gmx, uint32_
 // Process one lane chunk v[32] (all 64 lanes of the wave call this together: BLOCK uses shuffles).
 // Returns the per-lane scale value to store (BLOCK: fp32 bits; MX/MOSS: E8M0 byte) in `sc`.
 // BLOCK 1x128: the four chunks of a group sit in lanes l, l ^ G, l ^ 2G, l ^ 3G.
+// mx: the chunk's max |x| bits; mnm1: its min (|x| bits - 1), or nullptr to compute it from v (only
+// BLOCK's division guard uses it).
 template <int FMT, int MODE, bool BF16, int G = 1>
-__device__ __forceinline__ void process_chunk(const float* v, const UniformScale& u, uint32_t* out,
-                                              uint32_t& sc, uint32_t& chunk_max_out) {
-    const uint32_t mx = chunk_max<32>(v);
-    chunk_max_out = mx;
+__device__ __forceinline__ void process_chunk_mm(const float* v, uint32_t mx, const uint32_t* mnm1, const UniformScale& u,
+                                                 uint32_t* out, uint32_t& sc) {
     if (MODE == kModeBlock) {
         uint32_t gmx = mx;
         uint32_t o = (uint32_t)__shfl_xor((int)gmx, G, 64);
@@ -179,11 +179,19 @@ __device__ __forceinline__ void process_chunk(const float* v, const UniformScale
         gmx = max(gmx, o);
         float s = scale_from_amax<FMT>(__uint_as_float(gmx), 1.0f);
         float y = recip_rn(s);
-        cast_div<FMT, false, 32>(v, s, y, 0, divisor_ok(s) && dividends_ok(mx, chunk_min_m1<32>(v)), out);
+        const uint32_t mn = mnm1 ? *mnm1 : chunk_min_m1<32>(v);
+        cast_div<FMT, false, 32>(v, s, y, 0, divisor_ok(s) && dividends_ok(mx, mn), out);
         sc = __float_as_uint(s);
     } else {
         cast_group<FMT, MODE, BF16, 32>(v, mx, mx, u, out, sc);
     }
+}
+template <int FMT, int MODE, bool BF16, int G = 1>
+__device__ __forceinline__ void process_chunk(const float* v, const UniformScale& u, uint32_t* out,
+                                              uint32_t& sc, uint32_t& chunk_max_out) {
+    const uint32_t mx = chunk_max<32>(v);
+    chunk_max_out = mx;
+    process_chunk_mm<FMT, MODE, BF16, G>(v, mx, nullptr, u, out, sc);
 }
 
 __device__ __forceinline__ void store32(uint8_t* p, const uint32_t* w) {
@@ -224,10 +232,28 @@ __global__ __launch_bounds__(THREADS) void cast_rows_kernel(CastArgs a) {
         const int64_t r = gg / cpr, c = gg - r * cpr;
         const char* src = static_cast<const char*>(a.x) + (r * a.ld + c * 32) * esz;
         float v[32];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) load8<BF16>(src + j * 8 * esz, v + 8 * j);
         uint32_t out[8], sc = 0, cm = 0;
-        process_chunk<FMT, MODE, BF16>(v, u, out, sc, cm);
+        if constexpr (BF16) {
+            // max and min of |x| from the packed words (one 16-bit op per two values)
+            uint32_t w[16];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint4 q = reinterpret_cast<const uint4*>(src)[j];
+                w[4 * j] = q.x;
+                w[4 * j + 1] = q.y;
+                w[4 * j + 2] = q.z;
+                w[4 * j + 3] = q.w;
+            }
+#pragma unroll
+            for (int q = 0; q < 16; ++q) { v[2 * q] = bf16lo(w[q]); v[2 * q + 1] = bf16hi(w[q]); }
+            cm = bf16w_absmax<16>(w);
+            const uint32_t mn = bf16w_minm1<16>(w);
+            process_chunk_mm<FMT, MODE, BF16>(v, cm, &mn, u, out, sc);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) load8<BF16>(src + j * 8 * esz, v + 8 * j);
+            process_chunk<FMT, MODE, BF16>(v, u, out, sc, cm);
+        }
         if (valid) {
             store32(a.q + r * a.ldq + c * 32, out);
             if (MODE == kModeBlock) {
