@@ -138,14 +138,16 @@ __device__ __forceinline__ UniformScale uniform_scale(const CastArgs& a) {
 }
 
 // TENSOR / MX / MOSS cast of N values of one 32-group: gmx is the group's max |x| bits, lmx the
-// max of these N values (the division path is chosen per lane; the result does not depend on it).
+// max of these N values (the division path is chosen per lane; the result does not depend on it);
+// lmn, when given, their min (|x| bits - 1) for the division guard (else computed from v -- the
+// compiler evaluates it ahead of the per-lane branch, so callers holding packed words pass it).
 // Returns the E8M0 byte (MX, MOSS) in sc.
 template <int FMT, int MODE, bool BF16, int N>
 __device__ __forceinline__ void cast_group(const float* v, uint32_t gmx, uint32_t lmx, const UniformScale& u,
-                                           uint32_t* out, uint32_t& sc) {
+                                           uint32_t* out, uint32_t& sc, const uint32_t* lmn = nullptr) {
     if (MODE == kModeTensor) {
         if (BF16 && u.two && lmx < 0x7F800000u) cast_mul2<FMT, N>(v, u.yh, u.yl, out);
-        else cast_div<FMT, false, N>(v, u.s, u.y, 0, u.ok && dividends_ok(lmx, chunk_min_m1<N>(v)), out);
+        else cast_div<FMT, false, N>(v, u.s, u.y, 0, u.ok && dividends_ok(lmx, lmn ? *lmn : chunk_min_m1<N>(v)), out);
     } else if (MODE == kModeMX) {
         int e = mx_exponent<FMT>(__uint_as_float(gmx));
         cast_mx<FMT, N>(v, -e, lmx > 0x7F800000u, out);
@@ -158,7 +160,8 @@ __device__ __forceinline__ void cast_group(const float* v, uint32_t gmx, uint32_
         if (BF16 && u.two && e > -100 && divisor_ok(sg) && lmx < 0x7F800000u)
             cast_mul2<FMT, N>(v, __builtin_amdgcn_ldexpf(u.yh, -e), __builtin_amdgcn_ldexpf(u.yl, -e), out);
         else
-            cast_div<FMT, true, N>(v, u.s, u.y, -e, u.ok && dividends_ok(lmx, chunk_min_m1<N>(v)) && e > -100, out);
+            cast_div<FMT, true, N>(v, u.s, u.y, -e,
+                                   u.ok && dividends_ok(lmx, lmn ? *lmn : chunk_min_m1<N>(v)) && e > -100, out);
         sc = (uint32_t)(e + 127);
     }
 }
@@ -183,7 +186,7 @@ __device__ __forceinline__ void process_chunk_mm(const float* v, uint32_t mx, co
         cast_div<FMT, false, 32>(v, s, y, 0, divisor_ok(s) && dividends_ok(mx, mn), out);
         sc = __float_as_uint(s);
     } else {
-        cast_group<FMT, MODE, BF16, 32>(v, mx, mx, u, out, sc);
+        cast_group<FMT, MODE, BF16, 32>(v, mx, mx, u, out, sc, mnm1);
     }
 }
 template <int FMT, int MODE, bool BF16, int G = 1>
@@ -463,8 +466,8 @@ __global__ __launch_bounds__(kTileThreads) void cast_dual_run_kernel(CastArgs a)
 #pragma unroll
             for (int q = 0; q < 16; ++q) { v[2 * q] = bf16lo(wv[q]); v[2 * q + 1] = bf16hi(wv[q]); }
             uint32_t out[8], sc = 0;
-            const uint32_t cm = bf16w_absmax<16>(wv);
-            cast_group<FMT, MODE, true, 32>(v, cm, cm, u, out, sc);
+            const uint32_t cm = bf16w_absmax<16>(wv), mn = bf16w_minm1<16>(wv);
+            cast_group<FMT, MODE, true, 32>(v, cm, cm, u, out, sc, &mn);
             const int64_t r = band * 128 + rr;
             uint8_t* dst = a.q2 + r * a.ldq2 + c0 + 32 * h;
             *reinterpret_cast<uint4*>(dst + 16 * odd) = make_uint4(out[0], out[1], out[2], out[3]);
@@ -489,8 +492,8 @@ __global__ __launch_bounds__(kTileThreads) void cast_dual_run_kernel(CastArgs a)
 #pragma unroll
             for (int q = 0; q < 16; ++q) { v[2 * q] = bf16lo(pw[q]); v[2 * q + 1] = bf16hi(pw[q]); }
             uint32_t out[8], sc = 0;
-            const uint32_t cm = bf16w_absmax<16>(pw);
-            cast_group<FMT, MODE, true, 32>(v, cm, cm, u, out, sc);
+            const uint32_t cm = bf16w_absmax<16>(pw), mn = bf16w_minm1<16>(pw);
+            cast_group<FMT, MODE, true, 32>(v, cm, cm, u, out, sc, &mn);
             store32(a.q + (c0 + oc) * a.ldq + band * 128 + seg * 32, out);
             if (MODE == kModeMX || MODE == kModeMoss) tsc[oc][4 * (band - b0) + seg] = (uint8_t)sc;
         }
