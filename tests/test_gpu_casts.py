@@ -130,6 +130,24 @@ def test_mx_full_size_sampled(fq, orc):
         assert same(host(q)[rows], oq) and same(host(e)[rows], oe)
 
 
+def test_mx_past_2g_elements(fq, orc):
+    """A bf16 input of more than 2^31 elements (4 GiB): the row kernel's 64-bit indexing; rows around
+    element 2^31 and the last rows are checked."""
+    rows, cols = (1 << 20) + 64, 2048
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(13)
+    x = torch.randn(rows, cols, dtype=torch.bfloat16, device=DEV, generator=gen)
+    q, e, _, _ = fq.quantize(x, MX, E4M3)
+    boundary = (1 << 31) // cols
+    sel = np.unique(np.concatenate([np.arange(0, 16), np.arange(boundary - 32, boundary + 32), np.arange(rows - 32, rows)]))
+    st = torch.from_numpy(sel).to(DEV)
+    hx, hq, he = host(x[st]), host(q[st]), host(e[st])
+    del x, q, e
+    torch.cuda.empty_cache()
+    oq, oe = orc.quantize_mx(np.ascontiguousarray(hx), E4M3)
+    assert same(hq, oq) and same(he, oe)
+
+
 # ------------------------------------------------------------------ MOSS, six copies at full size
 def test_moss_full_size_six_copies(fq, orc):
     X, W, dY = workloads.moss_inputs()

@@ -201,3 +201,28 @@ def test_gemm_determinism_and_k_zero(fq, orc):
                        torch.zeros((16, 0), dtype=torch.uint8, device=DEV), E4M3, None,
                        torch.ones(1, device=DEV), torch.ones(1, device=DEV), out_dtype=OUT_F32)
     assert np.all(host(z) == 0.0)
+
+
+def test_gemm_operand_past_4gib(fq, orc):
+    """An A operand of more than 2^32 bytes: the dispatcher's fallback kernel, which addresses with
+    64-bit offsets.  Rows on both sides of the 4 GiB boundary and the last rows are checked."""
+    M, N, K = (1 << 20) + 256, 128, 4096
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(11)
+    A = torch.randint(0, 254, (M, K), dtype=torch.uint8, device=DEV, generator=gen)
+    A[A == 0x7F] = 0x7E                                      # no NaN codes
+    B, (hqb, _, hgb) = _quant_operand(fq, orc, workloads.random_matrix(12, N, K, 0.05), TENSOR, E4M3, None)
+    qb, _, gb = B
+    sa = torch.ones(1, dtype=torch.float32, device=DEV)
+    boundary = (1 << 32) // K                                 # first row wholly past 4 GiB
+    rows = np.unique(np.concatenate([np.arange(0, 64), np.arange(boundary - 64, boundary + 64),
+                                     np.arange(M - 64, M)]))
+    rt = torch.from_numpy(rows).to(DEV)
+    c32 = host(fq.scaled_gemm(TENSOR, A, E4M3, None, qb, E4M3, None, sa, gb, out_dtype=OUT_F32)[rt])
+    cbf = host(fq.scaled_gemm(TENSOR, A, E4M3, None, qb, E4M3, None, sa, gb, out_dtype=OUT_BF16)[rt])
+    Ad = orc.dequantize(TENSOR, host(A[rt]), E4M3, None, np.float32(1.0))
+    del A
+    torch.cuda.empty_cache()
+    Bd = orc.dequantize(TENSOR, hqb, E4M3, None, hgb)
+    Cref, D = orc.gemm_ref(Ad, Bd)
+    check_gemm(c32, cbf, Cref, D, chunk_max_sum(Ad, Bd), K, "A past 4 GiB", chain_prefix_abs(Ad, Bd))
