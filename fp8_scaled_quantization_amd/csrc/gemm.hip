@@ -13,11 +13,16 @@
 //           高效、精确的 FP8 LLM 训练 ...", sections 1 and 4);
 //   MOSS    as MX, then fl(S_A*S_B) once in the epilogue (same page, section 4, step 4).
 //
-// Accumulation.  gfx950's FP8 MFMA adds its products (and its C input) with only ~12-15 bits kept
-// below the largest term, so chaining one accumulator through MFMAs over a long K loses accuracy as
-// the accumulator grows.  Each 128-wide K step is therefore computed by MFMAs starting from zero
-// and added into a separate FP32 accumulator with VALU adds (a full-precision promotion every 128 K,
-// which BLOCK needs anyway for its per-block scales).
+// This file holds the dispatch (launch_sel, at the end) to the kernels that run the schemes: the
+// ping-pong kernels with 256 x 256 tiles (gemm_pp.cuh: TENSOR/MX/MOSS, whole-K accumulation in the
+// matrix core) and 256 x 128 tiles (gemm_ppb.cuh: block scaling, and smaller TENSOR/MX/MOSS
+// problems), the pipelined kernel for small problems (gemm_kernel.cuh), and the reference-tile
+// kernel below for what those do not cover (K not a multiple of 128, operands past 32-bit offsets).
+//
+// Reference-tile kernel.  Accumulation: gfx950's FP8 MFMA adds its products (and its C input) with
+// only ~12-15 bits kept below the largest term; this kernel computes each 128-wide K step by MFMAs
+// starting from zero and adds it into a separate FP32 accumulator with VALU adds (a full-precision
+// promotion every 128 K, which BLOCK needs anyway for its per-block scales).
 //
 // Tiling.  Block tile 128 x 128, K step 128 bytes, 256 threads = 4 waves in 2 x 2, wave tile
 // 64 x 64 = 4 x 4 MFMA tiles of 16 x 16.  A and B K-tiles are double-buffered in LDS (64 KiB) with a
@@ -261,7 +266,6 @@ static void launch_v2(const GemmArgs& g, hipStream_t st) {
     hipLaunchKernelGGL(kern, dim3((unsigned)(ntm * ntn)), dim3(64 * WM * WN), smem, st, g);
 }
 
-// Ping-pong kernel (gemm_pp.cuh): TENSOR, MX and MOSS with K % 128 == 0.
 // Ping-pong kernel with 256 x 128 tiles (gemm_ppb.cuh): every BLOCK / BLOCK_E8M0 problem, and
 // TENSOR/MX/MOSS problems too small for the 256 x 256 tiles.  K % 128 == 0.
 template <int MODE, int AFMT, int BFMT, bool OUT, bool E8, bool AST>
@@ -291,6 +295,7 @@ static void launch_ppb(const GemmArgs& g, hipStream_t st) {
     }
 }
 
+// Ping-pong kernel with 256 x 256 tiles (gemm_pp.cuh): TENSOR, MX and MOSS with K % 128 == 0.
 template <int MODE, int AFMT, int BFMT, bool OUT>
 static void launch_pp(const GemmArgs& g, hipStream_t st) {
     const int64_t ntm = (g.M + pp::BM - 1) / pp::BM, ntn = (g.N + pp::BN - 1) / pp::BN;
