@@ -296,6 +296,19 @@ static void launch_ppb(const GemmArgs& g, hipStream_t st) {
 }
 
 // Ping-pong kernel with 256 x 256 tiles (gemm_pp.cuh): TENSOR, MX and MOSS with K % 128 == 0.
+// CUs of the current device, read once per device
+static int64_t compute_units() {
+    static int64_t cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
 template <int MODE, int AFMT, int BFMT, bool OUT>
 static void launch_pp(const GemmArgs& g, hipStream_t st) {
     const int64_t ntm = (g.M + pp::BM - 1) / pp::BM, ntn = (g.N + pp::BN - 1) / pp::BN;
@@ -306,7 +319,14 @@ static void launch_pp(const GemmArgs& g, hipStream_t st) {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)(ntm * ntn)), dim3(512), smem, st, g);
+    // one workgroup per CU (the kernel's LDS and registers admit no second one), each looping over
+    // tiles; a grid smaller than the tile count is a multiple of 8 so that every workgroup's tiles
+    // stay on its XCD
+    const int64_t ntiles = ntm * ntn;
+    int64_t grid = compute_units();
+    grid -= grid % 8;
+    if (grid <= 0 || ntiles <= grid) grid = ntiles;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), smem, st, g);
 }
 
 static bool fits_u32(int64_t bytes) { return bytes >= 0 && bytes < ((int64_t)1 << 32); }

@@ -36,6 +36,14 @@
 // Global->LDS copies use buffer_load_dwordx4 ... lds (no VGPR staging; rows past M or N read zero
 // through the buffer range), with each 16-byte chunk c of tile row r stored at chunk position
 // c ^ (r & 7), which keeps both the copy writes and the fragment reads free of bank conflicts.
+//
+// Persistent grid.  With more tiles than CUs the grid has one workgroup per CU and each loops over
+// its tiles.  At a tile's end the workgroup sends the next tile's pipeline fill first and only then
+// the epilogue's 32 stores per wave, so the stores drain while the next tile's main loop starts
+// instead of holding the CU until they complete (vector-memory operations complete in issue order,
+// so the first waits of the next tile allow 32 more operations in flight).  Values that only the
+// tile boundary needs (C, ldc, M, N, the global factors, the lane index) are read again there rather
+// than kept in registers through the main loop, which uses nearly all of them.
 #pragma once
 #include "gemm_kernel.cuh"
 
@@ -122,48 +130,72 @@ __device__ __forceinline__ v4f mfma_sel(v8i a, v8i b, v4f c, int sa, int sb, int
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, AF, BF, 3, sa, 3, sb);
 }
 
+// A wave-uniform value the compiler must treat as new at this point: what is derived from it is
+// computed here, not hoisted out of the tile loop and kept live across the main loop.
+template <class T>
+__device__ __forceinline__ T fresh(T x) {
+    asm volatile("" : "+s"(x));
+    return x;
+}
+
+// The kernel's argument block, read through the scalar cache (constant address space) from a
+// pointer the compiler must treat as new, so that an argument needed only at a tile's end is loaded
+// there instead of occupying a scalar register through the main loop.
+typedef __attribute__((address_space(4))) const GemmArgs kargs_t;
+__device__ __forceinline__ kargs_t* kernel_args() {
+    return reinterpret_cast<kargs_t*>(fresh(reinterpret_cast<uint64_t>(__builtin_amdgcn_kernarg_segment_ptr())));
+}
+
 // One copy instruction: 8 tile rows starting at row r0 (64 rows of scale bytes for a scale quad).
 // The buffer descriptor's range ends at the operand's last row, and the row offset is part of the
 // range-checked per-lane offset, so rows past M or N read zero; the K offset goes into the
 // unchecked scalar offset.  The lane offset is formed by an asm add so that it is recomputed at
 // each copy rather than kept in a register per instruction.
-__device__ __forceinline__ void copy8(uint8_t* lds, rsrc_t rs, uint32_t voff0, uint32_t row_off, uint32_t koff) {
+__device__ __forceinline__ void copy8(uint32_t lds, rsrc_t rs, uint32_t voff0, uint32_t row_off, uint32_t koff) {
     uint32_t voff;
     asm volatile("v_add_u32 %0, %1, %2" : "=v"(voff) : "s"(row_off), "v"(voff0));
-    dma16(lds_addr(lds), rs, voff, koff);
+    dma16(lds, rs, voff, koff);
+}
+// The same with the LDS destination as a pointer into the dynamic allocation.
+__device__ __forceinline__ void copy8(uint8_t* lds, rsrc_t rs, uint32_t voff0, uint32_t row_off, uint32_t koff) {
+    copy8(lds_addr(lds), rs, voff0, row_off, koff);
 }
 
 // Wave wi: A rows 64 wi .. +64 of step ks into the stage of step s (8 copies).  ks = s except past
 // the last step, where the copies repeat the last step's data into a stage no step reads, so that
 // the main loop has no branches and the same wait counts in every iteration.
-__device__ __forceinline__ void copy_A(uint8_t* smem, int s, int ks, int wi, rsrc_t ra, uint32_t voffA, uint32_t lda) {
-    uint8_t* st = smem + (s & 1) * kStage;
+__device__ __forceinline__ void copy_A(uint32_t sbase, int s, int ks, int wi, rsrc_t ra, uint32_t voffA, uint32_t lda) {
+    const uint32_t st = sbase + (s & 1) * kStage;
     const uint32_t koff = (uint32_t)ks * BK;
+    uint32_t l = st + (uint32_t)(wi * 64) * BK, ro = (uint32_t)(wi * 64) * lda;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const uint32_t r0 = (uint32_t)(wi * 64 + j * 8);
-        copy8(st + r0 * BK, ra, voffA, r0 * lda, koff);
+        copy8(l, ra, voffA, ro, koff);
+        l = fresh(l + 8 * BK);
+        ro = fresh(ro + 8 * lda);
     }
 }
 // Wave wi: B rows base + 32 wi .. +32 of step ks into the stage of step s (4 copies); base 0 (B0)
 // or 128 (B1).
-__device__ __forceinline__ void copy_B(uint8_t* smem, int s, int ks, int base, int wi, rsrc_t rb, uint32_t voffB,
+__device__ __forceinline__ void copy_B(uint32_t sbase, int s, int ks, int base, int wi, rsrc_t rb, uint32_t voffB,
                                        uint32_t ldb) {
-    uint8_t* st = smem + (s & 1) * kStage + kA;
+    const uint32_t st = sbase + (s & 1) * kStage + kA;
     const uint32_t koff = (uint32_t)ks * BK;
+    uint32_t l = st + (uint32_t)(base + wi * 32) * BK, ro = (uint32_t)(base + wi * 32) * ldb;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const uint32_t r0 = (uint32_t)(base + wi * 32 + j * 8);
-        copy8(st + r0 * BK, rb, voffB, r0 * ldb, koff);
+        copy8(l, rb, voffB, ro, koff);
+        l = fresh(l + 8 * BK);
+        ro = fresh(ro + 8 * ldb);
     }
 }
 // Group 0, wave wi, every fourth step: two instructions of the scale quad for steps s .. s+3.
 // The K offset goes into the range-checked lane offset: when the K steps are not a multiple of 4
 // the last quad of a row ends past the row, and on the array's last row past its end, where the
 // buffer range turns the excess into zeros.
-__device__ __forceinline__ void copy_quad(uint8_t* smem, int s, int wi, rsrc_t rsa, rsrc_t rsb, uint32_t voffS,
+__device__ __forceinline__ void copy_quad(uint32_t sbase, int s, int wi, rsrc_t rsa, rsrc_t rsb, uint32_t voffS,
                                           uint32_t sc_row) {
-    uint8_t* sq = smem + kScBase + ((s >> 2) & 1) * kScQuad;
+    const uint32_t sq = sbase + kScBase + ((s >> 2) & 1) * kScQuad;
     const uint32_t voff = voffS + (uint32_t)s * 4;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -180,233 +212,322 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const int t = threadIdx.x, lane = t & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform: kept in SGPRs
+    const int wave = fresh(__builtin_amdgcn_readfirstlane(t >> 6));   // wave-uniform: kept in SGPRs
     const int grp = wave >> 2;
     const int wm = wave & 3, wn = grp;            // wave tile: rows 64 wm .. +64, cols 128 wn .. +128
     const int r16 = lane & 15, g4 = lane >> 4;
     const int64_t M = g.M, N = g.N;
-    const int64_t ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
-
-    // tile coordinates: undo the round-robin XCD dispatch, then walk groups of 8 tile-rows
-    int64_t b = blockIdx.x;
-    {
-        const int64_t nb = ntm * ntn;
-        if (nb % 8 == 0) b = (b % 8) * (nb / 8) + b / 8;
-    }
-    const int64_t per_group = 8 * ntn;
-    const int64_t gi = b / per_group, first_m = gi * 8;
-    const int64_t gm = min(ntm - first_m, (int64_t)8);
-    const int64_t in_grp = b - gi * per_group;
-    const int64_t m0 = (first_m + in_grp % gm) * BM, n0 = (in_grp / gm) * BN;
+    // the launcher admits operands of fewer than 2^32 bytes, so tile counts and byte offsets within
+    // an operand fit 32 bits
+    const uint32_t ntm_ = (uint32_t)((M + BM - 1) / BM), ntn_ = (uint32_t)((N + BN - 1) / BN);
+    const uint32_t ntiles = ntm_ * ntn_;
+    // Tile coordinates: undo the round-robin XCD dispatch, then walk groups of 8 tile-rows.  The
+    // grid is a multiple of 8 workgroups (or one per tile) and workgroup w takes tiles w, w + G,
+    // w + 2G, ... (G = gridDim.x), so tile % 8, the XCD, stays fixed and the tiles that one XCD
+    // runs at the same time are neighbours in the walk.
+    auto coords = [&](uint32_t tile, uint32_t& m0_, uint32_t& n0_) {
+        kargs_t* gk = kernel_args();
+        const uint32_t ntm = (uint32_t)((gk->M + BM - 1) / BM), ntn = (uint32_t)((gk->N + BN - 1) / BN);
+        const uint32_t ntiles = ntm * ntn;
+        uint32_t b = tile;
+        if (ntiles % 8 == 0) b = (b % 8) * (ntiles / 8) + b / 8;
+        const uint32_t per_group = 8 * ntn;
+        const uint32_t gi = b / per_group, first_m = gi * 8;
+        const uint32_t gm = min(ntm - first_m, 8u);
+        const uint32_t in_grp = b - gi * per_group;
+        // the division runs on the vector unit: bring the results back to scalar registers
+        m0_ = (uint32_t)__builtin_amdgcn_readfirstlane((int)((first_m + in_grp % gm) * BM));
+        n0_ = (uint32_t)__builtin_amdgcn_readfirstlane((int)((in_grp / gm) * BN));
+    };
     const int nk = (int)(g.K / BK);
     // global dequantisation factors (TENSOR: s_a, s_b; MOSS: S_A, S_B), read early through the
     // scalar cache; their product fl(s_a * s_b) scales the accumulators in the epilogue
-    float ga = 1.0f, gb = 1.0f;
-    if (MODE == kModeTensor || MODE == kModeMoss) {
-        ga = g2::load_uniform_f32(g.Aglobal);
-        gb = g2::load_uniform_f32(g.Bglobal);
-    }
 
+    // Buffer descriptors over whole operands: their ranges end at the last row, so rows past M or N
+    // read zero; a tile's row offset is part of the range-checked lane offset.
     const int64_t sc_row = 4 * (int64_t)nk;      // E8M0 bytes per row
-    const rsrc_t ra = make_rsrc(g.A + m0 * g.lda, (uint32_t)(max((int64_t)0, M - m0) * g.lda));
-    const rsrc_t rb = make_rsrc(g.B + n0 * g.ldb, (uint32_t)(max((int64_t)0, N - n0) * g.ldb));
+    const rsrc_t ra = make_rsrc(g.A, (uint32_t)(M * g.lda));
+    const rsrc_t rb = make_rsrc(g.B, (uint32_t)(N * g.ldb));
     rsrc_t rsa = rsrc_t{0u, 0u, 0u, 0u}, rsb = rsrc_t{0u, 0u, 0u, 0u};
     if (SCALED) {
-        rsa = make_rsrc(static_cast<const uint8_t*>(g.Ascale) + m0 * sc_row, (uint32_t)(max((int64_t)0, M - m0) * sc_row));
-        rsb = make_rsrc(static_cast<const uint8_t*>(g.Bscale) + n0 * sc_row, (uint32_t)(max((int64_t)0, N - n0) * sc_row));
+        rsa = make_rsrc(g.Ascale, (uint32_t)(M * sc_row));
+        rsb = make_rsrc(g.Bscale, (uint32_t)(N * sc_row));
     }
     // copy lanes: lane i of a copy instruction covers row r0 + i/8 at LDS chunk i%8, fetching global
-    // chunk (i%8) ^ (row & 7) (r0 is a multiple of 8); scale quads take one row per lane
+    // chunk (i%8) ^ (row & 7) (r0 is a multiple of 8); scale quads take one row per lane (waves 0-1
+    // of group 1 A rows, waves 2-3 B rows)
     const uint32_t ch = (uint32_t)(((lane & 7) ^ ((lane >> 3) & 7)) << 4);
-    const uint32_t voffA = (uint32_t)((lane >> 3) * g.lda) + ch;
-    const uint32_t voffB = (uint32_t)((lane >> 3) * g.ldb) + ch;
-    const uint32_t voffS = (uint32_t)(lane * sc_row);
     const uint32_t ulda = (uint32_t)g.lda, uldb = (uint32_t)g.ldb, usc = (uint32_t)sc_row;
     const int wi = wave & 3;
+    const uint32_t sbase = lds_addr(smem);   // LDS address of the dynamic allocation
 
     // fragment read offsets (loop invariant): row base of each 16-row subtile, swizzled chunks
     const uint32_t cLo = (uint32_t)((g4 ^ (r16 & 7)) << 4), cHi = (uint32_t)(((4 + g4) ^ (r16 & 7)) << 4);
     const uint32_t rowA = (uint32_t)((wm * 64 + r16) * BK), rowB = (uint32_t)((wn * 128 + r16) * BK);
 
-    v4f acc[4][8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    uint32_t tile = blockIdx.x, m0, n0;
+    coords(tile, m0, n0);
+    uint32_t voffA, voffB, voffS;
+    auto lane_offsets = [&](uint32_t tm, uint32_t tn) {
+        voffA = (uint32_t)(lane >> 3) * ulda + ch + tm * ulda;
+        voffB = (uint32_t)(lane >> 3) * uldb + ch + tn * uldb;
+        voffS = (uint32_t)lane * usc + (wi < 2 ? tm : tn) * usc;
+    };
+    lane_offsets(m0, n0);
 
-    // ---- prologue: group 1 sends A and B0 of step 0 and A of step 1; group 0 sends B1 of step 0
-    // and B0 of step 1 (afterwards it sends B1 of step k+1 in its memory phase for step k and B0
-    // of step k+2 after its MFMAs for step k; group 1 sends A of step k+2 in its memory phase)
+    // ---- a tile's pipeline fill: group 1 sends A and B0 of step 0 and A of step 1; group 0 sends
+    // B1 of step 0 and B0 of step 1 (afterwards it sends B1 of step k+1 in its memory phase for step
+    // k and B0 of step k+2 after its MFMAs for step k; group 1 sends A of step k+2 in its memory
+    // phase).  For every tile but the first it goes out before the previous tile's epilogue, whose
+    // stores then follow it in the wave's vector-memory queue.
     const int k1 = nk > 1 ? 1 : 0;
-    if (grp == 0) {
-        copy_B(smem, 0, 0, 128, wi, rb, voffB, uldb);
-        copy_B(smem, 1, k1, 0, wi, rb, voffB, uldb);
-        wait_vm<4>();
-    } else {
-        copy_A(smem, 0, 0, wi, ra, voffA, ulda);
-        copy_B(smem, 0, 0, 0, wi, rb, voffB, uldb);
-        if (SCALED) copy_quad(smem, 0, wi, rsa, rsb, voffS, usc);
-        copy_A(smem, 1, k1, wi, ra, voffA, ulda);
-        wait_vm<8>();
-    }
-    barrier();
+    auto fill = [&]() {
+        const uint32_t la = fresh(ulda), lb = fresh(uldb), ls = fresh(usc), sb0 = fresh(sbase);
+        if (grp == 0) {
+            copy_B(sb0, 0, 0, 128, wi, rb, voffB, lb);
+            copy_B(sb0, 1, k1, 0, wi, rb, voffB, lb);
+        } else {
+            copy_A(sb0, 0, 0, wi, ra, voffA, la);
+            copy_B(sb0, 0, 0, 0, wi, rb, voffB, lb);
+            if (SCALED) copy_quad(sb0, 0, wi, rsa, rsb, voffS, ls);
+            copy_A(sb0, 1, k1, wi, ra, voffA, la);
+        }
+    };
+    fill();
+    // kStores stores of the previous tile sit behind the fill: vector-memory operations complete in
+    // issue order, so a wait for the fill or older work must allow that many more in flight
+    constexpr int kStores = 32;
+    bool behind = false;
     v8i fa[4], fb[8];
-    if (grp == 1) {
-        // group 1 reads A of step 0 while group 0 has its first memory phase
-#pragma unroll
-        for (int i = 0; i < 4; ++i) fa[i] = frag(smem + rowA + i * 16 * BK, cLo, cHi);
-        barrier();
-    }
+    v4f acc[4][8];
 
-    int sca = 0, scb0 = 0, scb1 = 0;
-    for (int k = 0; k < nk; ++k) {
-        // ---- memory phase: scale words first, then fragment reads interleaved with this phase's
-        // copies (a copy may wait for the address unit; the LDS reads queued around it keep going)
-        uint32_t sw[12];
-        if (SCALED) {
-            const uint32_t* sq = reinterpret_cast<const uint32_t*>(smem + kScBase + ((k >> 2) & 1) * kScQuad);
-            const int qs = k & 3;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sw[i] = sq[(wm * 64 + i * 16 + r16) * 4 + qs];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) sw[4 + j] = sq[(BM + wn * 128 + j * 16 + r16) * 4 + qs];
+    for (;;) {
+        // next tile's coordinates, while the accumulators are dead
+        const uint32_t tile_n = tile + fresh(gridDim.x);
+        uint32_t m0n = 0, n0n = 0;
+        if (tile_n < ntiles) coords(tile_n, m0n, n0n);
+
+        if (grp == 0) {
+            if (behind) wait_vm<4 + kStores>();
+            else wait_vm<4>();
+        } else {
+            if (behind) wait_vm<8 + kStores>();
+            else wait_vm<8>();
         }
-        {
-            const uint8_t* sa = smem + (k & 1) * kStage;
-            const uint8_t* sb = sa + kA;
-            if (grp == 0) {
-                // A and B0 of step k; B1 of step k+1 (4 copies), one per three fragment reads
-                uint8_t* st = smem + ((k + 1) & 1) * kStage + kA;
-                const uint32_t koff = (uint32_t)min(k + 1, nk - 1) * BK;
-#pragma unroll
-                for (int q = 0; q < 12; ++q) {
-                    if (q % 3 == 0) {
-                        const uint32_t r0 = (uint32_t)(128 + wi * 32 + (q / 3) * 8);
-                        copy8(st + r0 * BK, rb, voffB, r0 * uldb, koff);
-                    }
-                    if (q < 4) fa[q] = frag(sa + rowA + q * 16 * BK, cLo, cHi);
-                    else fb[q - 4] = frag(sb + rowB + (q - 4) * 16 * BK, cLo, cHi);
-                }
-                // B1 of step k (sent one memory phase ago) lands before group 1 reads it next phase;
-                // newer: B0 of step k+1 (sent in the last compute phase, or the prologue) and this
-                // phase's B1
-                wait_vm<8>();
-            } else {
-                // B1 of step k; A of step k+2 (8 copies, one per fragment read) and the scale quad
-                uint8_t* st = smem + (k & 1) * kStage;
-                const uint32_t koff = (uint32_t)min(k + 2, nk - 1) * BK;
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const uint32_t r0 = (uint32_t)(wi * 64 + q * 8);
-                    copy8(st + r0 * BK, ra, voffA, r0 * ulda, koff);
-                    fb[q] = frag(sb + rowB + q * 16 * BK, cLo, cHi);
-                }
-                const bool quad = SCALED && k + 2 < nk && ((k + 2) & 3) == 0;
-                if (quad) copy_quad(smem, k + 2, wi, rsa, rsb, voffS, usc);
-                // A of step k+1 (sent one memory phase ago, or in the prologue) lands before group 0
-                // reads it next phase; this phase's copies may stay in flight
-                if (quad) wait_vm<10>();
-                else wait_vm<8>();
-            }
-        }
-        if (SCALED) {
-            // byte g4 of a row's word = the E8M0 scale of (row, group g4) for this step; four
-            // subtiles per register, picked in the MFMA by its byte select
-            const int sh = 8 * g4;
-            uint32_t pa = 0, pb0 = 0, pb1 = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pa |= ((sw[i] >> sh) & 0xFFu) << (8 * i);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) pb0 |= ((sw[4 + j] >> sh) & 0xFFu) << (8 * j);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) pb1 |= ((sw[8 + j] >> sh) & 0xFFu) << (8 * j);
-            sca = (int)pa;
-            scb0 = (int)pb0;
-            scb1 = (int)pb1;
-            // finish the packing here, in the memory phase, not after the barrier
-            asm volatile("" ::"v"(sca), "v"(scb0), "v"(scb1));
-        }
-        wait_lgkm0();
         barrier();
-        // ---- compute phase (group 1 also reads A of step k+1, row block by row block; past the
-        // last step it reads a stage it does not use)
-        const bool next_a = grp == 1;
-        const uint8_t* sn = smem + ((k + 1) & 1) * kStage;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (SCALED)
-                    acc[i][j] = mfma_sel<AFMT, BFMT>(fa[i], fb[j], acc[i][j], sca, j < 4 ? scb0 : scb1, i, j & 3);
-                else
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[i], fb[j], acc[i][j], AFMT, BFMT, 0, 0,
-                                                                                  0, 0);
-            }
-            if (next_a) {
-                // the eight MFMAs above are issued before fa[i] is overwritten
-                asm volatile("" ::"v"(acc[i][0]), "v"(acc[i][1]), "v"(acc[i][2]), "v"(acc[i][3]), "v"(acc[i][4]),
-                             "v"(acc[i][5]), "v"(acc[i][6]), "v"(acc[i][7]));
-                fa[i] = frag(sn + rowA + i * 16 * BK, cLo, cHi);
-            }
-        }
-        // every accumulator is read here, so all 32 MFMAs are issued before the barrier
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            asm volatile("" ::"v"(acc[i][0]), "v"(acc[i][1]), "v"(acc[i][2]), "v"(acc[i][3]), "v"(acc[i][4]),
-                         "v"(acc[i][5]), "v"(acc[i][6]), "v"(acc[i][7]));
-        if (grp == 0) {
-            // B0 of step k+2, into the stage group 0 finished reading last phase, sent after this
-            // phase's MFMAs: group 1's memory phase, which moves A, is the longer one
-            uint8_t* st = smem + (k & 1) * kStage + kA;
-            const uint32_t koff = (uint32_t)min(k + 2, nk - 1) * BK;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t r0 = (uint32_t)(wi * 32 + j * 8);
-                copy8(st + r0 * BK, rb, voffB, r0 * uldb, koff);
-            }
-            // B0 of step k+1 (sent in the last compute phase, or the prologue) lands before group 0
-            // reads it next phase; newer: B1 of step k+1 (this memory phase) and B0 of step k+2
-            wait_vm<8>();
+            for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        if (grp == 1) {
+            // group 1 reads A of step 0 while group 0 has its first memory phase
+#pragma unroll
+            for (int i = 0; i < 4; ++i) fa[i] = frag(smem + rowA + i * 16 * BK, cLo, cHi);
+            barrier();
         }
-        barrier();
-    }
-    if (grp == 0) barrier();          // matches group 1's extra barrier at the start
-    wait_vm0();                       // the last steps' repeated copies
 
-    // ---- epilogue
-    const float f = (MODE == kModeTensor || MODE == kModeMoss) ? ga * gb : 1.0f;
-    if (OUT_BF16 && m0 + BM <= M && n0 + BN <= N) {
-        // full tile: quad transposes and 8-byte stores (quad_transpose_bf16)
-        const int q = r16 & 3, c4 = r16 >> 2;
-        const uint32_t modd = 0u - (uint32_t)(q & 1), mhi = 0u - (uint32_t)(q >> 1);
-        uint16_t* const cw = static_cast<uint16_t*>(g.C) + (m0 + wm * 64) * g.ldc + n0 + wn * 128;
-        const uint32_t loff = (uint32_t)((4 * g4 + q) * g.ldc + 4 * c4);
+        int sca = 0, scb0 = 0, scb1 = 0;
+        for (int k = 0; k < nk; ++k) {
+            // in step 0 the copies waited for are the fill's, which are older than the stores
+            // (the test goes through fresh() so that the compiler does not peel the first step)
+            const bool st0 = behind && fresh(k) == 0;
+            // LDS bases of this step's stage and the other one, computed afresh in every step
+            const uint32_t sk = fresh(sbase + (k & 1) * kStage), sk1 = fresh(sbase + ((k + 1) & 1) * kStage);
+            // ---- memory phase: scale words first, then fragment reads interleaved with this phase's
+            // copies (a copy may wait for the address unit; the LDS reads queued around it keep going)
+            uint32_t sw[12];
+            if (SCALED) {
+                const uint32_t* sq = reinterpret_cast<const uint32_t*>(smem + kScBase + ((k >> 2) & 1) * kScQuad);
+                const int qs = k & 3;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint16_t* const ci = cw + (int64_t)i * 16 * g.ldc;
+                for (int i = 0; i < 4; ++i) sw[i] = sq[(wm * 64 + i * 16 + r16) * 4 + qs];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                *reinterpret_cast<uint2*>(ci + loff + j * 16) = quad_transpose_bf16(acc[i][j] * f, modd, mhi);
-        }
-    } else {
-        // partial tile or fp32 output: element by element, masked
-        const int64_t row0 = m0 + wm * 64 + 4 * g4, col0 = n0 + wn * 128 + r16;
+                for (int j = 0; j < 8; ++j) sw[4 + j] = sq[(BM + wn * 128 + j * 16 + r16) * 4 + qs];
+            }
+            {
+                const uint8_t* sa = smem + (k & 1) * kStage;
+                const uint8_t* sb = sa + kA;
+                if (grp == 0) {
+                    // A and B0 of step k; B1 of step k+1 (4 copies), one per three fragment reads
+                    const uint32_t st = sk1 + kA;
+                    const uint32_t koff = (uint32_t)min(k + 1, nk - 1) * BK;
+                    uint32_t l = st + (uint32_t)(128 + wi * 32) * BK, ro = (uint32_t)(128 + wi * 32) * uldb;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+                    for (int q = 0; q < 12; ++q) {
+                        if (q % 3 == 0) {
+                            copy8(l, rb, voffB, ro, koff);
+                            l = fresh(l + 8 * BK);
+                            ro = fresh(ro + 8 * uldb);
+                        }
+                        if (q < 4) fa[q] = frag(sa + rowA + q * 16 * BK, cLo, cHi);
+                        else fb[q - 4] = frag(sb + rowB + (q - 4) * 16 * BK, cLo, cHi);
+                    }
+                    // B1 of step k (sent one memory phase ago) lands before group 1 reads it next
+                    // phase; newer: B0 of step k+1 (sent in the last compute phase, or the fill) and
+                    // this phase's B1
+                    if (st0) wait_vm<8 + kStores>();
+                    else wait_vm<8>();
+                } else {
+                    // B1 of step k; A of step k+2 (8 copies, one per fragment read) and the scale quad
+                    const uint32_t st = sk;
+                    const uint32_t koff = (uint32_t)min(k + 2, nk - 1) * BK;
+                    uint32_t l = st + (uint32_t)(wi * 64) * BK, ro = (uint32_t)(wi * 64) * ulda;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int64_t col = col0 + j * 16;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int64_t row = row0 + i * 16 + e;
-                    if (row < M && col < N) {
-                        const float v = acc[i][j][e] * f;
-                        if (OUT_BF16) static_cast<uint16_t*>(g.C)[row * g.ldc + col] = g2::f32_to_bf16_rne(v);
-                        else static_cast<float*>(g.C)[row * g.ldc + col] = v;
+                    for (int q = 0; q < 8; ++q) {
+                        copy8(l, ra, voffA, ro, koff);
+                        l = fresh(l + 8 * BK);
+                        ro = fresh(ro + 8 * ulda);
+                        fb[q] = frag(sb + rowB + q * 16 * BK, cLo, cHi);
+                    }
+                    const bool quad = SCALED && k + 2 < nk && ((k + 2) & 3) == 0;
+                    if (quad) copy_quad(sbase, k + 2, wi, rsa, rsb, voffS, usc);
+                    // A of step k+1 (sent one memory phase ago, or in the fill) lands before group 0
+                    // reads it next phase; this phase's copies may stay in flight
+                    if (st0) {
+                        if (quad) wait_vm<10 + kStores>();
+                        else wait_vm<8 + kStores>();
+                    } else {
+                        if (quad) wait_vm<10>();
+                        else wait_vm<8>();
                     }
                 }
             }
+            if (SCALED) {
+                // byte g4 of a row's word = the E8M0 scale of (row, group g4) for this step; four
+                // subtiles per register, picked in the MFMA by its byte select
+                const int sh = 8 * g4;
+                uint32_t pa = 0, pb0 = 0, pb1 = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pa |= ((sw[i] >> sh) & 0xFFu) << (8 * i);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) pb0 |= ((sw[4 + j] >> sh) & 0xFFu) << (8 * j);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) pb1 |= ((sw[8 + j] >> sh) & 0xFFu) << (8 * j);
+                sca = (int)pa;
+                scb0 = (int)pb0;
+                scb1 = (int)pb1;
+                // finish the packing here, in the memory phase, not after the barrier
+                asm volatile("" ::"v"(sca), "v"(scb0), "v"(scb1));
+            }
+            wait_lgkm0();
+            barrier();
+            // ---- compute phase (group 1 also reads A of step k+1, row block by row block; past the
+            // last step it reads a stage it does not use)
+            const bool next_a = grp == 1;
+            const uint8_t* sn = smem + ((k + 1) & 1) * kStage;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if (SCALED)
+                        acc[i][j] = mfma_sel<AFMT, BFMT>(fa[i], fb[j], acc[i][j], sca, j < 4 ? scb0 : scb1, i, j & 3);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[i], fb[j], acc[i][j], AFMT, BFMT,
+                                                                                      0, 0, 0, 0);
+                }
+                if (next_a) {
+                    // the eight MFMAs above are issued before fa[i] is overwritten
+                    asm volatile("" ::"v"(acc[i][0]), "v"(acc[i][1]), "v"(acc[i][2]), "v"(acc[i][3]), "v"(acc[i][4]),
+                                 "v"(acc[i][5]), "v"(acc[i][6]), "v"(acc[i][7]));
+                    fa[i] = frag(sn + rowA + i * 16 * BK, cLo, cHi);
+                }
+            }
+            // every accumulator is read here, so all 32 MFMAs are issued before the barrier
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                asm volatile("" ::"v"(acc[i][0]), "v"(acc[i][1]), "v"(acc[i][2]), "v"(acc[i][3]), "v"(acc[i][4]),
+                             "v"(acc[i][5]), "v"(acc[i][6]), "v"(acc[i][7]));
+            if (grp == 0) {
+                // B0 of step k+2, into the stage group 0 finished reading last phase, sent after this
+                // phase's MFMAs: group 1's memory phase, which moves A, is the longer one
+                const uint32_t st = sk + kA;
+                const uint32_t koff = (uint32_t)min(k + 2, nk - 1) * BK;
+                uint32_t l = st + (uint32_t)(wi * 32) * BK, ro = (uint32_t)(wi * 32) * uldb;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    copy8(l, rb, voffB, ro, koff);
+                    l = fresh(l + 8 * BK);
+                    ro = fresh(ro + 8 * uldb);
+                }
+                // B0 of step k+1 (sent in the last compute phase, or the fill) lands before group 0
+                // reads it next phase; newer: B1 of step k+1 (this memory phase) and B0 of step k+2
+                if (st0) wait_vm<8 + kStores>();
+                else wait_vm<8>();
+            }
+            barrier();
         }
+        if (grp == 0) barrier();          // matches group 1's extra barrier at the start
+        // every wave's copies of this tile (the last steps repeat the last step's data) have landed
+        // before any wave refills the stages
+        wait_vm0();
+        barrier();
+        const bool more = tile_n < ntiles;
+        if (more) {
+            // move the lane offsets to the next tile (no lane index needs to stay live)
+            voffA += (m0n - m0) * ulda;
+            voffB += (n0n - n0) * uldb;
+            voffS += (wi < 2 ? m0n - m0 : n0n - n0) * usc;
+            fill();
+        }
+        // the epilogue's stores stay behind the fill
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- epilogue
+        // the epilogue's arguments are read again from the kernel argument segment, so that they
+        // do not occupy scalar registers through the main loop
+        kargs_t* ga_ = kernel_args();
+        const int64_t ldc = ga_->ldc, Me = ga_->M, Ne = ga_->N;
+        typedef __attribute__((address_space(1))) uint16_t gu16;
+        typedef __attribute__((address_space(1))) uint64_t gu64;
+        gu16* const C = (gu16*)ga_->C;
+        float f = 1.0f;
+        if (MODE == kModeTensor || MODE == kModeMoss) f = g2::load_uniform_f32(ga_->Aglobal) * g2::load_uniform_f32(ga_->Bglobal);
+        const bool full = OUT_BF16 && (int64_t)m0 + BM <= Me && (int64_t)n0 + BN <= Ne;
+        // lane index again from the hardware, rather than kept in a register through the main loop
+        const int le = (int)__lane_id(), er16 = le & 15, eg4 = le >> 4;
+        if (full) {
+            // full tile: quad transposes and kStores 8-byte stores (quad_transpose_bf16)
+            const int q = er16 & 3, c4 = er16 >> 2;
+            const uint32_t modd = 0u - (uint32_t)(q & 1), mhi = 0u - (uint32_t)(q >> 1);
+            gu16* const cw = C + ((int64_t)m0 + wm * 64) * ldc + n0 + wn * 128;
+            const uint32_t loff = (uint32_t)((4 * eg4 + q) * ldc + 4 * c4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                gu16* const ci = cw + (int64_t)i * 16 * ldc;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint2 w = quad_transpose_bf16(acc[i][j] * f, modd, mhi);
+                    *reinterpret_cast<gu64*>(ci + loff + j * 16) = (uint64_t)w.x | ((uint64_t)w.y << 32);
+                }
+            }
+        } else {
+            // partial tile or fp32 output: element by element, masked
+            const int64_t row0 = (int64_t)m0 + wm * 64 + 4 * eg4, col0 = (int64_t)n0 + wn * 128 + er16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int64_t col = col0 + j * 16;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int64_t row = row0 + i * 16 + e;
+                        if (row < Me && col < Ne) {
+                            const float v = acc[i][j][e] * f;
+                            if (OUT_BF16) C[row * ldc + col] = g2::f32_to_bf16_rne(v);
+                            else ((__attribute__((address_space(1))) float*)C)[row * ldc + col] = v;
+                        }
+                    }
+                }
+            }
+            // the masked path issues a varying number of stores: let them finish, so the next
+            // tile's waits count only its own copies
+            wait_vm0();
+        }
+        if (!more) break;
+        behind = full;
+        tile = tile_n;
+        m0 = m0n;
+        n0 = n0n;
     }
 }
 

@@ -171,8 +171,12 @@ def test_gemm_moss_forward_backward_full_size_sampled(fq, orc):
 # Shapes with enough 256 x 256 tiles (>= 192) to take the ping-pong kernel, with partial tiles in
 # M and N and K of one, two and five 128-wide steps (the copy pipeline's start-up and drain cases).
 # 256 x 256 ping-pong kernel (at least 192 tiles of 256 x 256), then the 256 x 128 one (fewer, but at
-# least 192 tiles of 256 x 128), with partial tiles and a partial last scale quad
-PINGPONG = [(3000, 4000, 128), (3000, 4000, 256), (2900, 4100, 640), (2900, 2100, 640), (4096, 2048, 1152)]
+# least 192 tiles of 256 x 128), with partial tiles and a partial last scale quad.  The last three
+# have more 256 x 256 tiles than a GPU has CUs, so workgroups loop over tiles: 288 tiles with
+# partial ones in M and N, 1024 partial-edged tiles of one K step and 1024 full tiles of two K steps
+# (each tile's pipeline fill goes out before the previous tile's stores).
+PINGPONG = [(3000, 4000, 128), (3000, 4000, 256), (2900, 4100, 640), (2900, 2100, 640), (4096, 2048, 1152),
+            (4000, 4500, 384), (8000, 8000, 128), (8192, 8192, 256)]
 
 
 @pytest.mark.parametrize("mode", [TENSOR, MX, MOSS])
