@@ -280,7 +280,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
     // k and B0 of step k+2 after its MFMAs for step k; group 1 sends A of step k+2 in its memory
     // phase).  For every tile but the first it goes out before the previous tile's epilogue, whose
     // stores then follow it in the wave's vector-memory queue.
-    const int k1 = nk > 1 ? 1 : 0;
+    const int k1 = min(nk - 1, 1);   // (nk >= 1; a scalar min, not a select the compiler would keep in a VGPR)
     auto fill = [&]() {
         const uint32_t la = fresh(ulda), lb = fresh(uldb), ls = fresh(usc), sb0 = fresh(sbase);
         if (grp == 0) {
