@@ -180,6 +180,25 @@ PINGPONG = [(3000, 4000, 128), (3000, 4000, 256), (2900, 4100, 640), (2900, 2100
 
 
 @pytest.mark.parametrize("mode", [TENSOR, MX, MOSS])
+def test_gemm_persistent_full(fq, orc, mode):
+    """Every output of a problem whose 272 tiles of 256 x 256 (17 x 16, the last row and column of
+    tiles partial) exceed the GPU's CUs, so that workgroups loop over tiles, compared in full."""
+    M, N, K = 4200, 4000, 256
+    xa = workloads.random_matrix(71, M, K, 2.0)
+    xb = workloads.random_matrix(72, N, K, 0.05)
+    A, (hqa, hsa, hga) = _quant_operand(fq, orc, xa, mode, E4M3, None)
+    B, (hqb, hsb, hgb) = _quant_operand(fq, orc, xb, mode, E4M3, None)
+    Ad = _deq(orc, mode, hqa, hsa, hga, E4M3, (1, 128))
+    Bd = _deq(orc, mode, hqb, hsb, hgb, E4M3, (1, 128))
+    Cref, D = orc.gemm_ref(Ad, Bd)
+    E = chunk_max_sum(Ad, Bd)
+    Sg = chain_prefix_abs(Ad, Bd)
+    C32 = host(_run(fq, mode, A, E4M3, B, E4M3, OUT_F32))
+    Cbf = host(_run(fq, mode, A, E4M3, B, E4M3, OUT_BF16))
+    check_gemm(C32, Cbf, Cref, D, E, K, "persistent mode %d %dx%dx%d" % (mode, M, N, K), Sg)
+
+
+@pytest.mark.parametrize("mode", [TENSOR, MX, MOSS])
 @pytest.mark.parametrize("M,N,K", PINGPONG)
 @pytest.mark.parametrize("fmts", [(E4M3, E4M3), (E5M2, E4M3)])
 def test_gemm_pingpong_ragged_sampled(fq, orc, mode, M, N, K, fmts):
