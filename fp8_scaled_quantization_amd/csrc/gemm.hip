@@ -15,7 +15,7 @@
 //
 // This file holds the dispatch (launch_sel, at the end) to the kernels that run the schemes: the
 // ping-pong kernels with 256 x 256 tiles (gemm_pp.cuh: TENSOR/MX/MOSS, whole-K accumulation in the
-// matrix core) and 256 x 128 tiles (gemm_ppb.cuh: block scaling, and smaller TENSOR/MX/MOSS
+// matrix core; a persistent grid of one workgroup per CU when there are more tiles) and 256 x 128 tiles (gemm_ppb.cuh: block scaling, and smaller TENSOR/MX/MOSS
 // problems), the pipelined kernel for small problems (gemm_kernel.cuh), and the reference-tile
 // kernel below for what those do not cover (K not a multiple of 128, operands past 32-bit offsets).
 //

@@ -228,9 +228,9 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
     auto coords = [&](uint32_t tile, uint32_t& m0_, uint32_t& n0_) {
         kargs_t* gk = kernel_args();
         const uint32_t ntm = (uint32_t)((gk->M + BM - 1) / BM), ntn = (uint32_t)((gk->N + BN - 1) / BN);
-        const uint32_t ntiles = ntm * ntn;
+        const uint32_t nt = ntm * ntn;
         uint32_t b = tile;
-        if (ntiles % 8 == 0) b = (b % 8) * (ntiles / 8) + b / 8;
+        if (nt % 8 == 0) b = (b % 8) * (nt / 8) + b / 8;
         const uint32_t per_group = 8 * ntn;
         const uint32_t gi = b / per_group, first_m = gi * 8;
         const uint32_t gm = min(ntm - first_m, 8u);
@@ -240,8 +240,6 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
         n0_ = (uint32_t)__builtin_amdgcn_readfirstlane((int)((in_grp / gm) * BN));
     };
     const int nk = (int)(g.K / BK);
-    // global dequantisation factors (TENSOR: s_a, s_b; MOSS: S_A, S_B), read early through the
-    // scalar cache; their product fl(s_a * s_b) scales the accumulators in the epilogue
 
     // Buffer descriptors over whole operands: their ranges end at the last row, so rows past M or N
     // read zero; a tile's row offset is part of the range-checked lane offset.
@@ -480,6 +478,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
         typedef __attribute__((address_space(1))) uint16_t gu16;
         typedef __attribute__((address_space(1))) uint64_t gu64;
         gu16* const C = (gu16*)ga_->C;
+        // global dequantisation factors (TENSOR: s_a, s_b; MOSS: S_A, S_B) through the scalar cache;
+        // their product fl(s_a * s_b) scales the accumulators
         float f = 1.0f;
         if (MODE == kModeTensor || MODE == kModeMoss) f = g2::load_uniform_f32(ga_->Aglobal) * g2::load_uniform_f32(ga_->Bglobal);
         const bool full = OUT_BF16 && (int64_t)m0 + BM <= Me && (int64_t)n0 + BN <= Ne;
