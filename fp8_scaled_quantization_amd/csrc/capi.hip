@@ -27,6 +27,7 @@ int check_launch(const char* what) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // Per-device result of the architecture check (up to 64 devices).
 int g_arch_ok[64];   // 0 unknown, 1 gfx950, -1 other
@@ -97,6 +98,8 @@ int fp8_quantize(int mode, int fmt, const void* x, int in_dtype, int64_t rows, i
         return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: amax_out is required when the scale is derived (scale_is_input=0)");
     if (cols % 8 || ld % 8 || !aligned16(x))
         return fail(FP8Q_ERR_UNSUPPORTED, "fp8_quantize: needs cols %% 8 == 0, ld %% 8 == 0 and a 16-byte aligned x");
+    if (!aligned4(tensor_scale) || !aligned4(amax_out) || (mode == FP8Q_BLOCK && !aligned4(scales)))
+        return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: fp32 scale and amax pointers must be 4-byte aligned");
     (void)R;
     int rc = check_device();
     if (rc) return rc;
@@ -263,6 +266,10 @@ int fp8_scaled_gemm(int mode, const uint8_t* A, int afmt, const void* Ascale, co
                     "required for BLOCK, BLOCK_E8M0, MX and MOSS");
     if (K > 0 && (K % 16 || lda % 16 || ldb % 16 || !aligned16(A) || !aligned16(B)))
         return fail(FP8Q_ERR_UNSUPPORTED, "fp8_scaled_gemm: needs K, lda, ldb multiples of 16 and 16-byte aligned A, B");
+    // scale arrays are read in 4-byte words, except UE8M0 weight-block scales (read byte by byte)
+    if (!aligned4(Aglobal) || !aligned4(Bglobal) || !aligned4(Ascale) || (mode != FP8Q_BLOCK_E8M0 && !aligned4(Bscale)))
+        return fail(FP8Q_ERR_UNSUPPORTED, "fp8_scaled_gemm: Ascale, Aglobal, Bglobal and (except for BLOCK_E8M0) Bscale "
+                    "must be 4-byte aligned");
     int rc = check_device();
     if (rc) return rc;
     fp8q::GemmArgs g{};

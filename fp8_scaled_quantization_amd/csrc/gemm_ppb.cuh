@@ -104,9 +104,14 @@ __device__ __forceinline__ uint32_t block_scale_word(const void* base, int64_t i
                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) << 32);
     return *(cptr)(u & ~(uint64_t)3);
 }
+// The byte of an E8M0 scale sits at the low two bits of its own address within the aligned word
+// (the scale array itself need not be 4-byte aligned).
 template <bool E8>
-__device__ __forceinline__ float block_scale_value(uint32_t w, int64_t i) {
-    if (E8) return __builtin_amdgcn_ldexpf(1.0f, (int)((w >> (8 * (uint32_t)(i & 3))) & 0xFFu) - 127);
+__device__ __forceinline__ float block_scale_value(uint32_t w, const void* base, int64_t i) {
+    if (E8) {
+        const uint32_t sh = 8u * (uint32_t)((reinterpret_cast<uint64_t>(base) + (uint64_t)i) & 3u);
+        return __builtin_amdgcn_ldexpf(1.0f, (int)((w >> sh) & 0xFFu) - 127);
+    }
     return __uint_as_float(w);
 }
 
@@ -229,7 +234,7 @@ __global__ __launch_bounds__(512, 1) void gemm_ppb_kernel(GemmArgs g) {
         // BLOCK: the block-scale products of this step, fl(sx * sw)
         float rs[16];
         if (BLOCKED) {
-            const float sw = block_scale_value<E8>(swraw, wrow + k);
+            const float sw = block_scale_value<E8>(swraw, g.Bscale, wrow + k);
 #pragma unroll
             for (int i = 0; i < 16; ++i) rs[i] = (AST ? s_static : sx[i]) * sw;
         }

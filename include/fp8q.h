@@ -126,6 +126,8 @@ int fp8_amax(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld
  *   scaling: nothing clips unless the block holds Inf).  (128,128) is the UE8M0 weight scheme.
  *
  * Limits (FP8Q_ERR_UNSUPPORTED otherwise): cols % 8 == 0, ld % 8 == 0 and a 16-byte aligned x.
+ * fp32 pointers (tensor_scale, amax_out, FP8Q_BLOCK scales) must be 4-byte aligned
+ * (FP8Q_ERR_INVALID_ARG otherwise); E8M0 scale arrays may start at any byte.
  * Any ldq >= K works (ldq % 16 == 0 with a 16-byte aligned q selects the vectorized kernels).
  * Ragged group tails (K not a multiple of the group) are handled with ceil semantics.
  */
@@ -198,7 +200,9 @@ int fp8_history_update(float* history, int64_t len, const float* amax_new,
  * Accumulation: FP8Q_TENSOR, FP8Q_MX and FP8Q_MOSS keep the whole K sum in the FP8 matrix
  * instruction's FP32 accumulator; FP8Q_BLOCK reduces each 128-wide K chunk from zero and adds its
  * scaled FP32 partial into an FP32 accumulator.
- * Limits (FP8Q_ERR_UNSUPPORTED otherwise): K % 16 == 0, lda/ldb % 16 == 0, 16-byte aligned A, B.
+ * Limits (FP8Q_ERR_UNSUPPORTED otherwise): K % 16 == 0, lda/ldb % 16 == 0, 16-byte aligned A, B;
+ * Ascale, Aglobal, Bglobal and Bscale 4-byte aligned (the kernels read scale arrays in 4-byte
+ * words), except the UE8M0 Bscale of FP8Q_BLOCK_E8M0, which may start at any byte.
  * M, N, K need not be multiples of any tile size.
  */
 int fp8_scaled_gemm(int mode, const uint8_t* A, int afmt, const void* Ascale,

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 from fp8_scaled_quantization_amd import workloads
-from tests.gpu_util import DEV, chain_prefix_abs, check_gemm, chunk_max_sum, host, same, sample_pairs, to_dev
+from tests.gpu_util import DEV, check_gemm, check_gemm_large, host, reference_terms, same, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -166,7 +166,16 @@ def test_block_dequantize_bit_exact(fq, orc, mode, out, shape, fmt):
 
 
 # ------------------------------------------------------------------ GEMM: UE8M0 weights, static activations
-def _gemm_case(fq, orc, M, N, K, wmode, static_a, seed, sampled):
+def _offset_view(t, offset):
+    """A copy of t that starts `offset` bytes into a fresh byte buffer (a view the caller might
+    hand over when its scales sit inside a larger allocation)."""
+    buf = torch.zeros(t.numel() * t.element_size() + 16, dtype=torch.uint8, device=t.device)
+    v = buf[offset:offset + t.numel() * t.element_size()].view(t.dtype).view(t.shape)
+    v.copy_(t)
+    return v
+
+
+def _gemm_case(fq, orc, M, N, K, wmode, static_a, seed, sampled, scale_offset=0):
     X = workloads.random_matrix(seed, M, K, 1.0)
     W = workloads.random_matrix(seed + 1, N, K, 0.02)
     if static_a:
@@ -184,6 +193,9 @@ def _gemm_case(fq, orc, M, N, K, wmode, static_a, seed, sampled):
         Ascale, Aglobal = sx, None
     qw, sw, _, _ = fq.quantize(to_dev(W), wmode, E4M3, block=(128, 128))
     hqw, hsw = host(qw), host(sw)
+    if scale_offset:
+        sw = _offset_view(sw, scale_offset)
+        assert sw.data_ptr() % 4 == scale_offset % 4
     deqB = lambda rows: orc.dequantize(wmode, np.ascontiguousarray(hqw[rows]), E4M3,
                                        np.ascontiguousarray(hsw[rows // 128]), block=(1, 128))
     C32 = torch.empty((M, N), dtype=torch.float32, device=DEV)
@@ -192,16 +204,10 @@ def _gemm_case(fq, orc, M, N, K, wmode, static_a, seed, sampled):
     fq.fp8_scaled_gemm(wmode, qx, E4M3, Ascale, qw, E4M3, sw, Aglobal, None, Cbf, OUT_BF16)
     label = "mode %d static %d %dx%dx%d" % (wmode, static_a, M, N, K)
     if sampled:
-        pairs = sample_pairs(M, N, 2048, seed)
-        rows, cols = np.unique(pairs[:, 0]), np.unique(pairs[:, 1])
-        Ad, Bd = deqA(rows), deqB(cols)
-        local = np.stack([np.searchsorted(rows, pairs[:, 0]), np.searchsorted(cols, pairs[:, 1])], 1).astype(np.int64)
-        Cref, D = orc.gemm_ref(Ad, Bd, local)
-        E = chunk_max_sum(Ad, Bd, local)
-        return check_gemm(host(C32)[pairs[:, 0], pairs[:, 1]], host(Cbf)[pairs[:, 0], pairs[:, 1]], Cref, D, E, K, label)
+        return check_gemm_large(orc, C32, Cbf, deqA, deqB, M, N, K, seed, label, promoted=True)
     Ad, Bd = deqA(np.arange(M)), deqB(np.arange(N))
-    Cref, D = orc.gemm_ref(Ad, Bd)
-    return check_gemm(host(C32), host(Cbf), Cref, D, chunk_max_sum(Ad, Bd), K, label)
+    Cref, D, E, _ = reference_terms(orc, Ad, Bd, promoted=True)
+    return check_gemm(host(C32), host(Cbf), Cref, D, E, K, label)
 
 
 @pytest.mark.parametrize("wmode", [BLOCK, BLOCK_E8M0])
@@ -211,8 +217,27 @@ def test_block_gemm_weight_and_activation_scale_kinds(fq, orc, wmode, static_a, 
     _gemm_case(fq, orc, M, N, K, wmode, static_a, M + N + K, sampled=False)
 
 
+@pytest.mark.parametrize("offset", [1, 2, 3])
+@pytest.mark.parametrize("M,N,K", [(256, 384, 1024), (300, 260, 256), (200, 136, 384)])
+def test_block_gemm_ue8m0_weight_scales_at_any_byte(fq, orc, offset, M, N, K):
+    """UE8M0 weight-block scales handed over at a byte offset of 1-3 within a word: the kernels
+    must pick each scale's own byte, whatever the array's alignment."""
+    _gemm_case(fq, orc, M, N, K, BLOCK_E8M0, False, M + N + K + offset, sampled=False, scale_offset=offset)
+
+
+def test_gemm_misaligned_word_scales_are_refused(fq):
+    """Scale arrays the kernels read in 4-byte words (MX/MOSS E8M0 rows, fp32 block scales) must
+    be 4-byte aligned: an offset view is refused with FP8Q_ERR_UNSUPPORTED, not misread."""
+    A = torch.zeros((256, 256), dtype=torch.uint8, device=DEV)
+    e = torch.full((256, 8), 127, dtype=torch.uint8, device=DEV)
+    C = torch.empty((256, 256), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(fq.Fp8qError) as ei:
+        fq.fp8_scaled_gemm(MX, A, E4M3, _offset_view(e, 1), A, E4M3, e, None, None, C, OUT_BF16)
+    assert ei.value.code == -2
+
+
 @pytest.mark.parametrize("wmode,static_a", [(BLOCK_E8M0, False), (BLOCK, True), (BLOCK_E8M0, True)])
-def test_block_gemm_fine_grained_full_size_sampled(fq, orc, wmode, static_a):
+def test_block_gemm_fine_grained_full_size(fq, orc, wmode, static_a):
     _gemm_case(fq, orc, 4096, 2048, 7168, wmode, static_a, 3, sampled=True)
 
 
@@ -262,6 +287,5 @@ def test_delayed_forward_backward_steps(fq, orc):
             Cbf = fq.scaled_gemm(TENSOR, dq[ka][wa], fmts[ka], None, dq[kb][wb], fmts[kb], None,
                                  dq[ka][2], dq[kb][2], out_dtype=OUT_BF16)
             Ad, Bd = deq(ka, wa), deq(kb, wb)
-            Cref, D = orc.gemm_ref(Ad, Bd)
-            check_gemm(host(C32), host(Cbf), Cref, D, chunk_max_sum(Ad, Bd), K, "%s t=%d" % (name, t),
-                       chain_prefix_abs(Ad, Bd))
+            Cref, D, E, Sg = reference_terms(orc, Ad, Bd)
+            check_gemm(host(C32), host(Cbf), Cref, D, E, K, "%s t=%d" % (name, t), Sg)
