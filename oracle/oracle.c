@@ -515,6 +515,62 @@ void orc_gemm_ref(const double* A, const double* B, int64_t M, int64_t N, int64_
         }
 }
 
+/* The same product with the two further sums that size the rounding error of a GEMM which
+ * reduces K in chunks of `chunk` (the matrix instruction's K width), per (m, n):
+ *   E[m][n]   = sum over chunks of max_{k in chunk} |A[m][k] * B[n][k]|,
+ *   Sig[m][n] = sum over chunks j of |S_{j-1}|, with S_{j-1} the sum of the products of all chunks
+ *               before chunk j (the running sum a whole-K accumulation feeds back as its input),
+ * both in fp64.  C and D are exactly those of orc_gemm_ref.  The last chunk may be short. */
+static void gemm_terms_one(const double* a, const double* b, int64_t K, int64_t chunk, double* c_out,
+                           double* d_out, double* e_out, double* s_out) {
+    double c = 0.0, d = 0.0, e = 0.0, sig = 0.0, prefix = 0.0;
+    for (int64_t k0 = 0; k0 < K; k0 += chunk) {
+        int64_t k1 = k0 + chunk < K ? k0 + chunk : K;
+        double part = 0.0, mx = 0.0;
+        for (int64_t k = k0; k < k1; ++k) {
+            double p = a[k] * b[k];
+            c += p;
+            d += fabs(p);
+            part += p;
+            if (fabs(p) > mx) mx = fabs(p);
+        }
+        e += mx;
+        sig += fabs(prefix);
+        prefix += part;
+    }
+    *c_out = c;
+    *d_out = d;
+    *e_out = e;
+    *s_out = sig;
+}
+
+void orc_gemm_ref_terms(const double* A, const double* B, int64_t M, int64_t N, int64_t K, int64_t chunk,
+                        const int64_t* pairs, int64_t npairs, double* C, double* D, double* E, double* Sig) {
+    if (pairs) {
+        #pragma omp parallel for schedule(dynamic, 64)
+        for (int64_t i = 0; i < npairs; ++i) {
+            int64_t m = pairs[2 * i], n = pairs[2 * i + 1];
+            gemm_terms_one(A + m * K, B + n * K, K, chunk, C + i, D + i, E + i, Sig + i);
+        }
+        return;
+    }
+    /* the longer axis is the parallel (outer) one, so a few rows against many columns (or the
+     * reverse) reads each long operand's rows once */
+    if (M >= N) {
+        #pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t m = 0; m < M; ++m)
+            for (int64_t n = 0; n < N; ++n)
+                gemm_terms_one(A + m * K, B + n * K, K, chunk, C + m * N + n, D + m * N + n, E + m * N + n,
+                               Sig + m * N + n);
+    } else {
+        #pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t m = 0; m < M; ++m)
+                gemm_terms_one(A + m * K, B + n * K, K, chunk, C + m * N + n, D + m * N + n, E + m * N + n,
+                               Sig + m * N + n);
+    }
+}
+
 /* ---------------------------------------------------------------- SNR -------- */
 
 /* SNR in dB = 10 log10( sum x^2 / sum (x - xhat)^2 ), fp64; +inf when the noise is zero.

@@ -60,6 +60,7 @@ def lib():
             "orc_delayed_step": (None, [P, I, I64, I64, I64, I, I, P, P, I64, P, I64, P]),
             "orc_dequantize": (None, [I, P, I, I64, I64, I64, P, I64, I64, P, P]),
             "orc_gemm_ref": (None, [P, P, I64, I64, I64, P, I64, P, P]),
+            "orc_gemm_ref_terms": (None, [P, P, I64, I64, I64, I64, P, I64, P, P, P, P]),
             "orc_snr_db": (D, [P, P, I64]),
             "orc_quantize_block_e8m0": (None, [P, I, I64, I64, I64, I, I64, I64, I, P, I64, P]),
             "orc_scales_f32_to_e8m0": (I64, [P, I64, P]),
@@ -298,6 +299,29 @@ def gemm_ref(A: np.ndarray, B: np.ndarray, pairs: np.ndarray | None = None):
     D = np.empty(n, np.float64)
     lib().orc_gemm_ref(_p(A), _p(B), M, N, K, _p(pairs), n, _p(C), _p(D))
     return C, D
+
+
+def gemm_ref_terms(A: np.ndarray, B: np.ndarray, pairs: np.ndarray | None = None, chunk: int = 128):
+    """gemm_ref's C and D plus the error-size sums of a K-chunked accumulation: E (per chunk the
+    largest |product|, summed) and Sigma (per chunk |sum of all earlier chunks|, summed).
+    Returns (C, D, E, Sigma), full matrices or 1-D over `pairs`."""
+    A = np.ascontiguousarray(A, np.float64)
+    B = np.ascontiguousarray(B, np.float64)
+    M, K = A.shape
+    N, K2 = B.shape
+    assert K == K2 and chunk > 0
+    if pairs is None:
+        out = [np.empty((M, N), np.float64) for _ in range(4)]
+        lib().orc_gemm_ref_terms(_p(A), _p(B), M, N, K, chunk, None, 0, *(_p(o) for o in out))
+        return tuple(out)
+    pairs = np.ascontiguousarray(pairs, np.int64)
+    assert pairs.ndim == 2 and pairs.shape[1] == 2
+    assert pairs.size == 0 or (pairs[:, 0].min() >= 0 and pairs[:, 0].max() < M and pairs[:, 1].min() >= 0
+                               and pairs[:, 1].max() < N)
+    n = pairs.shape[0]
+    out = [np.empty(n, np.float64) for _ in range(4)]
+    lib().orc_gemm_ref_terms(_p(A), _p(B), M, N, K, chunk, _p(pairs), n, *(_p(o) for o in out))
+    return tuple(out)
 
 
 def snr_db(x: np.ndarray, xhat: np.ndarray) -> float:

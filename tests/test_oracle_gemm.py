@@ -122,3 +122,42 @@ def test_snr_ordering_on_workload_like_data(orc):
         snr_g = orc.snr_db(x, orc.dequantize(BLOCK, qg, fmt, sg, None, block=(1, 128)))
         snr_m = orc.snr_db(x, orc.dequantize(MOSS, qm, fmt, em, S))
         assert snr_m >= snr_t and snr_g >= snr_t
+
+
+@pytest.mark.parametrize("K,chunk", [(384, 128), (300, 128), (96, 32), (130, 64), (7, 128)])
+def test_gemm_ref_terms_match_their_definitions(orc, K, chunk):
+    """The chunked error-size sums against a direct numpy statement of their definitions (pad K
+    with zero products to whole chunks; E adds each chunk's largest |product|; Sigma adds |sum of
+    all earlier chunks|), full and over sampled pairs; C and D equal gemm_ref's bit for bit."""
+    rng = np.random.default_rng(K + chunk)
+    M, N = 9, 11
+    A = rng.standard_normal((M, K)) * np.exp(rng.uniform(-3, 3, (M, 1)))
+    B = rng.standard_normal((N, K))
+    nck = -(-K // chunk)
+    Ap = np.pad(A, ((0, 0), (0, nck * chunk - K))).reshape(M, 1, nck, chunk)
+    Bp = np.pad(B, ((0, 0), (0, nck * chunk - K))).reshape(1, N, nck, chunk)
+    prod = Ap * Bp
+    E_want = np.abs(prod).max(axis=3).sum(axis=2)
+    part = prod.sum(axis=3)
+    before = np.concatenate([np.zeros((M, N, 1)), np.cumsum(part, axis=2)[:, :, :-1]], axis=2)
+    S_want = np.abs(before).sum(axis=2)
+    C, D, E, S = orc.gemm_ref_terms(A, B, chunk=chunk)
+    C0, D0 = orc.gemm_ref(A, B)
+    assert np.array_equal(C, C0) and np.array_equal(D, D0)
+    assert np.allclose(E, E_want, rtol=1e-15, atol=0)
+    assert np.allclose(S, S_want, rtol=1e-12, atol=1e-12 * D.max())
+    pairs = np.stack([rng.integers(0, M, 40), rng.integers(0, N, 40)], 1)
+    Cp, Dp, Ep, Sp = orc.gemm_ref_terms(A, B, pairs, chunk=chunk)
+    idx = (pairs[:, 0], pairs[:, 1])
+    assert np.array_equal(Cp, C[idx]) and np.array_equal(Dp, D[idx])
+    assert np.array_equal(Ep, E[idx]) and np.array_equal(Sp, S[idx])
+    if nck == 1:
+        assert np.all(S == 0.0)
+
+
+def test_gemm_ref_terms_hand_values(orc):
+    """Two chunks of two: products (3, -5 | 2, 1) give E = 5 + 2, Sigma = 0 + |3 - 5|, C = 1, D = 11."""
+    A = np.array([[3.0, -5.0, 2.0, 1.0]])
+    B = np.ones((1, 4))
+    C, D, E, S = orc.gemm_ref_terms(A, B, chunk=2)
+    assert (C[0, 0], D[0, 0], E[0, 0], S[0, 0]) == (1.0, 11.0, 7.0, 2.0)
