@@ -267,6 +267,46 @@ def test_moss_invariants(orc, fmt):
                     assert Fraction(float(S)) * Fraction(2) ** (k - 1) < Fraction(float(s_i[r, j]))
 
 
+def _moss_local_exponents(x32: np.ndarray, S: np.float32, fmt) -> np.ndarray:
+    """Smallest e in [-127, 0] with S * 2^e >= s_i, s_i = fl32(amax_i / MAX) per 32-group (0 when
+    none), by exact float64 comparisons (S * 2^e is exact in float64 over this range)."""
+    am = np.abs(x32.reshape(x32.shape[0], -1, 32)).max(axis=2).astype(np.float32)
+    s_i = (am / np.float32(MAX[fmt])).astype(np.float64)
+    e = np.zeros(s_i.shape, np.int64)
+    S64 = float(S)
+    for k in range(-1, -128, -1):                      # lower e while S * 2^k still covers s_i
+        ok = (e == k + 1) & (np.ldexp(S64, k) >= s_i)
+        e[ok] = k
+    return e
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("s_factor", [1.0, 1.7, 3.0, 2.0 ** 12, 0.5])
+def test_moss_bytes_by_library_recomputation(orc, fmt, s_factor):
+    """MOSS elements and E8M0 bytes for a general global factor S, recomputed with torch: the
+    local exponents by exact comparison, then an IEEE fp32 divide by S, an exact power-of-two
+    multiply by 2^-e_i, a clamp to +-MAX and torch's RNE cast.  S factors above 1 leave headroom
+    (many groups get e_i < 0, some values land in FP8 subnormals); 0.5 puts the tensor max past
+    S * MAX, where e_i = 0 and the clamp saturates."""
+    rng = np.random.default_rng(int(s_factor * 7) + fmt)
+    x = rng.standard_normal((96, 256)) * np.exp(rng.uniform(-6, 6, (96, 1)))
+    x[:, 5] *= 50.0
+    if fmt == E5M2:
+        x *= 1e-3
+    xb = workloads.to_bf16_bits(x.astype(np.float32))
+    x32 = f32(xb)
+    S = np.float32(np.float32(np.abs(x32).max()) / np.float32(MAX[fmt]) * np.float32(s_factor))
+    q, e = orc.quantize_moss_given(xb, fmt, S)
+    e_want = _moss_local_exponents(x32, S, fmt)
+    assert np.array_equal(e.astype(np.int64) - 127, e_want)
+    v = torch.from_numpy(x32) / torch.tensor(S, dtype=torch.float32)
+    up = torch.from_numpy(np.repeat(np.ldexp(1.0, -e_want), 32, axis=1).astype(np.float32))
+    v = (v * up).clamp(-MAX[fmt], MAX[fmt])
+    want = v.to(TORCH_FMT[fmt]).view(torch.uint8).numpy()
+    assert np.array_equal(q, want)
+    assert (e_want < 0).any() and (s_factor >= 1.0 or (e_want == 0).any())
+
+
 def test_moss_dominates_per_tensor(orc):
     """With the same global S, each MOSS element is at least as close to fl(x/S) as the
     per-tensor element, so MOSS's SNR is never below per-tensor's."""
