@@ -15,7 +15,12 @@ reduction of W, the delayed-scaling history merge, UE8M0 128x128 weight quantiza
 dequantization, and the block GEMM with UE8M0 weight scales and with a static activation scale.
 Each cast is also timed alone, cold (input from HBM) and warm ("quantize_cold_warm").
 The headline value is the step's total GEMM flops (2 M N K per GEMM) divided by the step time,
-i.e. scaled-GEMM TFLOP/s including every quantization the path performs.
+i.e. scaled-GEMM TFLOP/s including every quantization the path performs.  "per_config" gives each
+workload's GEMM flops over the summed time of all its launches beside the ceiling the two
+rooflines allow (GEMM flops at the FP8 MFMA peak plus its cast bytes at the HBM peak).  The
+oracle leg ("cpu_baseline", skipped with --no-cpu-baseline) times the CPU oracle per workload on a
+bounded sample and, outside that timing, reports the quantization SNR ("snr_db") of the MX and
+MOSS operands the timed steps wrote.
 
 The timed steps are replays of HIP graphs captured from the same library calls (one graph per
 delayed-scaling step index, since that input changes with the step); --no-graph times eager
@@ -154,7 +159,8 @@ def main():
     w4 = dict(A=dbf16(A4), B=dbf16(B4))
     X5, W5, G5 = wl.moss_inputs()
     w5 = dict(X=dbf16(X5), W=dbf16(W5), G=dbf16(G5))
-    host_inputs = dict(a1=a1, b1=b1, X3=X3, W3=W3, A4=A4, B4=B4, X5=X5, W5=W5, G5=G5)
+    A2h, B2h, _ = wl.delayed_inputs(0)
+    host_inputs = dict(a1=a1, b1=b1, A2=A2h, B2=B2h, X3=X3, W3=W3, A4=A4, B4=B4, X5=X5, W5=W5, G5=G5)
     gen_s = time.time() - t0
 
     # ---------------- outputs and state, allocated once (the library never allocates)
@@ -278,6 +284,27 @@ def main():
     per["h2"] = dict(ms=round(timer.mean_ms("h2"), 5))
     quant_ms = sum(timer.mean_ms(k) * qcalls[k] for k in qbytes)
     quant_gbs = sum(qbytes.values()) / (quant_ms * 1e-3) / 1e9
+    # each workload's GEMM flops over the time of all of its launches (casts, state updates,
+    # GEMMs), beside the ceiling both rooflines allow: flops / (flops / MFMA peak + cast bytes / HBM peak)
+    configs = {"per-tensor 16x32x64": (["q1"], ["g1"], []), "delayed 1024x2048x1024": (["q2"], ["g2"], ["h2"]),
+               "fine-grained 4096x7168x2048": (["q3x", "q3w"], ["g3"], []),
+               "MXFP8 8192^3": (["q4"], ["g4"], []), "MOSS fwd+bwd 16384x4096x4096": (["q5"], ["g5"], [])}
+    per_config = {}
+    for name, (qs, gs, extra) in configs.items():
+        fl = sum(gemm_flops[k] * launches[k] for k in gs)
+        ms = sum(timer.mean_ms(k) * qcalls[k] for k in qs) + sum(timer.mean_ms(k) * launches[k] for k in gs) + \
+            sum(timer.mean_ms(k) for k in extra)
+        by = sum(qbytes[k] for k in qs)
+        ideal_s = fl / (PEAK_FP8_TFLOPS * 1e12) + by / (PEAK_HBM_GBS * 1e9)
+        per_config[name] = {"ms": round(ms, 5), "tflops_incl_quantize": round(fl / (ms * 1e-3) / 1e12, 2),
+                            "pct_fp8_peak": round(100 * fl / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 2),
+                            "ceiling_pct_fp8_peak": round(100 * fl / ideal_s / 1e12 / PEAK_FP8_TFLOPS, 2)}
+    w_only = timer.mean_ms("q3x") + timer.mean_ms("g3")
+    per_config["fine-grained 4096x7168x2048"]["weights_prequantized"] = {
+        "ms": round(w_only, 5), "tflops_incl_quantize": round(gemm_flops["g3"] / (w_only * 1e-3) / 1e12, 2),
+        "ceiling_pct_fp8_peak": round(100 * gemm_flops["g3"] / (gemm_flops["g3"] / (PEAK_FP8_TFLOPS * 1e12) +
+                                                                 qbytes["q3x"] / (PEAK_HBM_GBS * 1e9)) / 1e12 /
+                                      PEAK_FP8_TFLOPS, 2)}
     # dominant kernel: the GEMM launch with the largest total time per step
     dom = max(gemm_flops, key=lambda k: timer.mean_ms(k) * launches[k])
     dom_ms = timer.mean_ms(dom)
@@ -307,11 +334,12 @@ def main():
         "ms_per_step_eager": round(eager_ms, 4),
         "pct_fp8_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
         "quantize_gbs": round(quant_gbs, 1), "quantize_pct_hbm_peak": round(100 * quant_gbs / PEAK_HBM_GBS, 2),
-        "roofline": roofline, "per_kernel": per, "quantize_cold_warm": cold_warm, "next_rows": next_rows,
+        "roofline": roofline, "per_config": per_config, "per_kernel": per, "quantize_cold_warm": cold_warm,
+        "next_rows": next_rows,
         "input_gen_s": round(gen_s, 1),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(host_inputs)
+        out["cpu_baseline"], out["snr_db"] = oracle_leg(host_inputs, o, torch)
     print(json.dumps(out), flush=True)
 
 
@@ -387,14 +415,40 @@ def measure_next(torch, fq, o, w3, w5, reps):
         torch.cuda.synchronize()
         return s.elapsed_time(e) / reps
 
+    def graph_timed(fn, n=50, replays=10):
+        """Device time per call: n calls captured in one HIP graph, replayed back to back, so that
+        no host launch cost is included (what remains per call is the kernel and its dispatch)."""
+        fn()
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(n):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(replays):
+            g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / (replays * n)
+
     W5, W3, X3 = w5["W"], w3["W"], w3["X"]
     amax = torch.zeros(1, dtype=torch.float32, device=dev)
     state = torch.zeros(2, dtype=torch.float32, device=dev)
     sc = torch.zeros(1, dtype=torch.float32, device=dev)
     fq.fp8_amax(W5, amax)
     fq.fp8_auto_scale(state, True, amax, 1e-4, E4M3, sc)
-    jit_ms = timed(lambda: (fq.fp8_amax(W5, amax), fq.fp8_auto_scale(state, True, amax, 1e-4, E4M3, sc)))
-    auto_ms = timed(lambda: fq.fp8_auto_scale(state, False, None, 1e-4, E4M3, sc))
+    jit_fn = lambda: (fq.fp8_amax(W5, amax), fq.fp8_auto_scale(state, True, amax, 1e-4, E4M3, sc))
+    auto_fn = lambda: fq.fp8_auto_scale(state, False, None, 1e-4, E4M3, sc)
+    jit_ms = timed(jit_fn)
+    auto_ms = timed(auto_fn)
+    jit_dev_ms = graph_timed(jit_fn)
+    auto_dev_ms = graph_timed(auto_fn)
     h1 = torch.zeros(1024, dtype=torch.float32, device=dev)
     h2 = torch.rand(1024, dtype=torch.float32, device=dev)
     s1, s2 = torch.ones(1, device=dev), torch.ones(1, device=dev)
@@ -418,6 +472,10 @@ def measure_next(torch, fq, o, w3, w5, reps):
     return {
         "auto_scale_us": round(auto_ms * 1e3, 2),
         "jit_amax_plus_scale_us": round(jit_ms * 1e3, 2),
+        "auto_scale_us_device": round(auto_dev_ms * 1e3, 2),
+        "jit_amax_plus_scale_us_device": round(jit_dev_ms * 1e3, 2),
+        "timing": "*_us: back-to-back eager launches (host launch rate); *_us_device: 50 calls in one HIP graph, "
+                  "replayed (device time per call)",
         "jit_tensor": "MOSS W 4096x4096 bf16",
         "history_merge_1024_us": round(merge_ms * 1e3, 2),
         "ue8m0_quantize_w_2048x7168": {"ms": round(qe_ms, 5), "gbs": round(wbytes_q / (qe_ms * 1e-3) / 1e9, 1),
@@ -437,50 +495,91 @@ def measure_next(torch, fq, o, w3, w5, reps):
     }
 
 
-def cpu_baseline(h):
-    """The CPU oracle timed on a bounded sample of the same step: every workload's quantization of a
-    row sample (all rows for the small workloads) and its fp64 GEMM for a sample of output rows
-    and columns; throughput in the metric's unit (GEMM TFLOP/s incl. quantize)."""
+def oracle_leg(h, o, torch):
+    """The CPU oracle timed on the host's cores over a bounded sample of each workload (its
+    quantization of sampled rows, or of the whole tensor where small, and its fp64 GEMM over the
+    sampled rows and columns), per workload and in total, in the metric's unit (GEMM TFLOP/s incl.
+    quantize); then, outside that timing, the quantization SNR of the step's own GPU output (the
+    MX and MOSS operands the timed steps wrote), dequantized exactly by the oracle."""
     import oracle.oracle as orc
+    from fp8_scaled_quantization_amd import workloads as wl
     lib = orc.lib()   # noqa: F841  (loads and, if needed, builds the oracle)
     cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
-    flops = 0.0
-    t0 = time.time()
-    # per-tensor current, whole workload
-    qa, sa = orc.quantize_tensor_current(h["a1"], 0)
-    qb, sb = orc.quantize_tensor_current(h["b1"], 0, transpose=True)
-    orc.gemm_ref(orc.dequantize(0, qa, 0, None, sa), orc.dequantize(0, qb, 0, None, sb))
-    flops += 2 * 16 * 64 * 32
+    per = {}
     r = 3072  # sampled rows of each operand for the large workloads
-    # fine-grained: r rows of X and one 128-row block of W, GEMM r x 128 x 7168
-    qx, sx = orc.quantize_block(np.ascontiguousarray(h["X3"][:r]), 0, 1, 128)
-    qw, sw = orc.quantize_block(np.ascontiguousarray(h["W3"][:128]), 0, 128, 128)
-    orc.gemm_ref(orc.dequantize(1, qx, 0, sx, None, block=(1, 128)), orc.dequantize(1, qw, 0, sw, None, block=(128, 128)))
-    flops += 2 * r * 128 * 7168
-    # MX: r rows of A and B, GEMM r x r x 8192
-    qa, ea = orc.quantize_mx(np.ascontiguousarray(h["A4"][:r]), 0)
-    qb, eb = orc.quantize_mx(np.ascontiguousarray(h["B4"][:r]), 0)
-    orc.gemm_ref(orc.dequantize(2, qa, 0, ea), orc.dequantize(2, qb, 0, eb))
-    flops += 2 * r * r * 8192
-    # MOSS: global factors over the whole tensors, then r-row samples of each copy and the 3 GEMMs
-    S = {n: orc.compute_scale(orc.amax(h[k]), f, 1.0) for n, k, f in (("X", "X5", 0), ("W", "W5", 0), ("G", "G5", 1))}
-    qX, eX = orc.quantize_moss_given(np.ascontiguousarray(h["X5"][:r]), 0, S["X"])
-    qW, eW = orc.quantize_moss_given(np.ascontiguousarray(h["W5"][:r]), 0, S["W"])
-    qG, eG = orc.quantize_moss_given(np.ascontiguousarray(h["G5"][:r]), 1, S["G"])
-    qWT, eWT = orc.quantize_moss_given(np.ascontiguousarray(h["W5"][:, :r]), 0, S["W"], transpose=True)
-    qGT, eGT = orc.quantize_moss_given(np.ascontiguousarray(h["G5"][:, :r]), 1, S["G"], transpose=True)
-    qXT, eXT = orc.quantize_moss_given(np.ascontiguousarray(h["X5"][:, :r]), 0, S["X"], transpose=True)
-    d = lambda q, e, f, s: orc.dequantize(3, q, f, e, s)
-    orc.gemm_ref(d(qX, eX, 0, S["X"]), d(qW, eW, 0, S["W"]))
-    orc.gemm_ref(d(qG, eG, 1, S["G"]), d(qWT, eWT, 0, S["W"]))
-    orc.gemm_ref(d(qGT, eGT, 1, S["G"]), d(qXT, eXT, 0, S["X"]))
-    flops += 2 * r * r * 4096 * 2 + 2 * r * r * 16384
-    secs = time.time() - t0
-    return {"value": round(flops / secs / 1e12, 8), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "seconds": round(secs, 2),
-            "sample": ("oracle quantize + fp64 GEMM: whole per-tensor workload; 3072-row samples of the fine-grained "
-                       "(x one 128-row weight block), MX and all six MOSS copies (global factors over whole "
-                       "tensors), GEMMs over those rows/columns; delayed workload not sampled")}
+
+    def timed(name, flops, sample, fn):
+        t0 = time.time()
+        fn()
+        secs = time.time() - t0
+        per[name] = {"tflops": round(flops / secs / 1e12, 8), "seconds": round(secs, 3), "gemm_flop": flops,
+                     "sample": sample}
+
+    def per_tensor():
+        qa, sa = orc.quantize_tensor_current(h["a1"], 0)
+        qb, sb = orc.quantize_tensor_current(h["b1"], 0, transpose=True)
+        orc.gemm_ref(orc.dequantize(0, qa, 0, None, sa), orc.dequantize(0, qb, 0, None, sb))
+    timed("per-tensor 16x32x64", 2 * 16 * 64 * 32, "whole workload", per_tensor)
+
+    rd = 256
+    def delayed():
+        scale_a, scale_b = np.ones(1, np.float32), np.ones(1, np.float32)
+        ha, hb = np.zeros(1024, np.float32), np.zeros(1024, np.float32)
+        qa, _ = orc.delayed_step(h["A2"], 0, scale_a, ha)
+        qb, _ = orc.delayed_step(h["B2"], 0, scale_b, hb, transpose=True)
+        orc.gemm_ref(orc.dequantize(0, np.ascontiguousarray(qa[:rd]), 0, None, scale_a[0]),
+                     orc.dequantize(0, qb, 0, None, scale_b[0]))
+    timed("delayed 1024x2048x1024", 2 * rd * 1024 * 2048,
+          "one step: both whole casts and history updates, GEMM of %d rows x all 1024 columns" % rd, delayed)
+
+    def fine():
+        qx, sx = orc.quantize_block(np.ascontiguousarray(h["X3"][:r]), 0, 1, 128)
+        qw, sw = orc.quantize_block(np.ascontiguousarray(h["W3"][:128]), 0, 128, 128)
+        orc.gemm_ref(orc.dequantize(1, qx, 0, sx, None, block=(1, 128)),
+                     orc.dequantize(1, qw, 0, sw, None, block=(128, 128)))
+    timed("fine-grained 4096x7168x2048", 2 * r * 128 * 7168,
+          "%d rows of X, one 128-row weight block, their %d x 128 GEMM" % (r, r), fine)
+
+    def mx():
+        qa, ea = orc.quantize_mx(np.ascontiguousarray(h["A4"][:r]), 0)
+        qb, eb = orc.quantize_mx(np.ascontiguousarray(h["B4"][:r]), 0)
+        orc.gemm_ref(orc.dequantize(2, qa, 0, ea), orc.dequantize(2, qb, 0, eb))
+    timed("MXFP8 8192^3", 2 * r * r * 8192, "%d rows of A and of B, their %d x %d GEMM" % (r, r, r), mx)
+
+    def moss():
+        S = {n: orc.compute_scale(orc.amax(h[k]), f, 1.0) for n, k, f in (("X", "X5", 0), ("W", "W5", 0), ("G", "G5", 1))}
+        qX, eX = orc.quantize_moss_given(np.ascontiguousarray(h["X5"][:r]), 0, S["X"])
+        qW, eW = orc.quantize_moss_given(np.ascontiguousarray(h["W5"][:r]), 0, S["W"])
+        qG, eG = orc.quantize_moss_given(np.ascontiguousarray(h["G5"][:r]), 1, S["G"])
+        qWT, eWT = orc.quantize_moss_given(np.ascontiguousarray(h["W5"][:, :r]), 0, S["W"], transpose=True)
+        qGT, eGT = orc.quantize_moss_given(np.ascontiguousarray(h["G5"][:, :r]), 1, S["G"], transpose=True)
+        qXT, eXT = orc.quantize_moss_given(np.ascontiguousarray(h["X5"][:, :r]), 0, S["X"], transpose=True)
+        d = lambda q, e, f, s: orc.dequantize(3, q, f, e, s)
+        orc.gemm_ref(d(qX, eX, 0, S["X"]), d(qW, eW, 0, S["W"]))
+        orc.gemm_ref(d(qG, eG, 1, S["G"]), d(qWT, eWT, 0, S["W"]))
+        orc.gemm_ref(d(qGT, eGT, 1, S["G"]), d(qXT, eXT, 0, S["X"]))
+    timed("MOSS fwd+bwd 16384x4096x4096", 2 * r * r * 4096 * 2 + 2 * r * r * 16384,
+          "global factors over whole tensors, %d-row samples of all six copies, the three GEMMs over them" % r, moss)
+
+    flops = sum(v["gemm_flop"] for v in per.values())
+    secs = sum(v["seconds"] for v in per.values())
+    baseline = {"value": round(flops / secs / 1e12, 8), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                "seconds": round(secs, 2), "per_config": per,
+                "sample": ("oracle quantize + fp64 GEMM over a bounded sample of every workload (see per_config); "
+                           "value = sampled GEMM flops over the summed oracle time")}
+
+    # quantization SNR (dB, fp64 over whole tensors) of the operands the GPU step quantized
+    def snr(bits, mode, q, e, fmt, S=None):
+        xhat = orc.dequantize(mode, q.cpu().numpy(), fmt, e.cpu().numpy(), S)
+        return round(orc.snr_db(wl.bf16_bits_to_f32(bits), xhat), 3)
+
+    S5 = {n: np.float32(o["S5" + n].item()) for n in ("X", "W", "G")}
+    snr_db = {"MXFP8 A 8192x8192 (MX)": snr(h["A4"], 2, o["q4a"], o["e4a"], 0),
+              "MXFP8 B 8192x8192 (MX)": snr(h["B4"], 2, o["q4b"], o["e4b"], 0),
+              "MOSS X 16384x4096 (MOSS, E4M3)": snr(h["X5"], 3, o["q5X"], o["e5X"], 0, S5["X"]),
+              "MOSS W 4096x4096 (MOSS, E4M3)": snr(h["W5"], 3, o["q5W"], o["e5W"], 0, S5["W"]),
+              "MOSS dY 16384x4096 (MOSS, E5M2)": snr(h["G5"], 3, o["q5G"], o["e5G"], 1, S5["G"])}
+    return baseline, snr_db
 
 
 if __name__ == "__main__":
