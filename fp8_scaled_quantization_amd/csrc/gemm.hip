@@ -36,6 +36,7 @@
 #include "gemm_kernel.cuh"
 #include "gemm_pp.cuh"
 #include "gemm_ppb.cuh"
+#include "gemm_pps.cuh"
 #include "kernels.h"
 
 namespace fp8q {
@@ -326,6 +327,21 @@ static void launch_pp(const GemmArgs& g, hipStream_t st) {
     int64_t grid = compute_units();
     grid -= grid % 8;
     if (grid <= 0 || ntiles <= grid) grid = ntiles;
+    const int64_t nk = g.K / pp::BK;
+    if constexpr (OUT) {
+        // workgroups with several tiles run them as one stream of K steps (gemm_pps.cuh)
+        if (ntiles > grid && nk % 4 == 0 && nk >= pps::kMinSteps) {
+            auto skern = pps::gemm_pps_kernel<MODE, AFMT, BFMT>;
+            static bool sattr_set = false;
+            if (!sattr_set) {
+                (void)hipFuncSetAttribute(reinterpret_cast<const void*>(skern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                          (int)smem);
+                sattr_set = true;
+            }
+            hipLaunchKernelGGL(skern, dim3((unsigned)grid), dim3(512), smem, st, g);
+            return;
+        }
+    }
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), smem, st, g);
 }
 

@@ -94,8 +94,8 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // columns per lane: lane (g4, r16 = 4 c4 + q) gets row 4 g4 + q, columns 4 c4 .. 4 c4 + 3, which it
 // stores with one 8-byte write (each row's 32 bytes come from four lanes).  modd and mhi are the
 // lane-constant masks 0 - (q & 1) and 0 - (q >> 1): the selections are bit selects, not branches.
-__device__ __forceinline__ uint2 quad_transpose_bf16(v4f v, uint32_t modd, uint32_t mhi) {
-    const uint32_t w0 = pack_bf16(v[0], v[1]), w1 = pack_bf16(v[2], v[3]);   // rows (0,1), (2,3)
+// Input: the packed words w0 = bf16 rows (0, 1) and w1 = rows (2, 3) of the lane's column.
+__device__ __forceinline__ uint2 quad_transpose_words(uint32_t w0, uint32_t w1, uint32_t modd, uint32_t mhi) {
     // swap with lane q^1: even lanes collect rows 0 and 2, odd lanes rows 1 and 3, of two adjacent
     // columns
     const uint32_t s1 = bitsel(modd, (w0 & 0xFFFFu) | (w1 << 16), (w0 >> 16) | (w1 & 0xFFFF0000u));
@@ -105,6 +105,10 @@ __device__ __forceinline__ uint2 quad_transpose_bf16(v4f v, uint32_t modd, uint3
     // swap with lane q^2: lane q ends with row q, columns 0-1 and 2-3 of the quad
     const uint32_t r2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)bitsel(mhi, x0, x1), 0x4E, 0xF, 0xF, false);   // [2,3,0,1]
     return make_uint2(bitsel(mhi, r2, x0), bitsel(mhi, x1, r2));
+}
+// The same from the four fp32 values of the lane's column (rounded to bf16 first).
+__device__ __forceinline__ uint2 quad_transpose_bf16(v4f v, uint32_t modd, uint32_t mhi) {
+    return quad_transpose_words(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), modd, mhi);
 }
 
 __device__ __forceinline__ v8i frag(const uint8_t* row, uint32_t lo, uint32_t hi) {

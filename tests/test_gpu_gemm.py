@@ -201,6 +201,25 @@ def test_gemm_persistent_full(fq, orc, mode):
 
 
 @pytest.mark.parametrize("mode", [TENSOR, MX, MOSS])
+@pytest.mark.parametrize("M,N,K", [(4200, 4000, 1536), (4096, 4608, 1024)])
+def test_gemm_stream_full(fq, orc, mode, M, N, K):
+    """Every output of problems run by the streaming 256 x 256 kernel (more tiles than CUs, K steps
+    a multiple of 4 and at least 8): 272 tiles with partial ones in M and N, so that some
+    workgroups run two tiles and the rest one, with 12 K steps (an odd number of scale quads per
+    tile, so the quad ring entry alternates from tile to tile); and 288 full tiles of 8 K steps."""
+    xa = workloads.random_matrix(M + 3 * K, M, K, 2.0)
+    xb = workloads.random_matrix(N + 5 * K, N, K, 0.05)
+    A, (hqa, hsa, hga) = _quant_operand(fq, orc, xa, mode, E4M3, None)
+    B, (hqb, hsb, hgb) = _quant_operand(fq, orc, xb, mode, E4M3, None)
+    Ad = _deq(orc, mode, hqa, hsa, hga, E4M3, (1, 128))
+    Bd = _deq(orc, mode, hqb, hsb, hgb, E4M3, (1, 128))
+    Cref, D, E, Sg = reference_terms(orc, Ad, Bd)
+    C32 = host(_run(fq, mode, A, E4M3, B, E4M3, OUT_F32))
+    Cbf = host(_run(fq, mode, A, E4M3, B, E4M3, OUT_BF16))
+    check_gemm(C32, Cbf, Cref, D, E, K, "stream mode %d %dx%dx%d" % (mode, M, N, K), Sg)
+
+
+@pytest.mark.parametrize("mode", [TENSOR, MX, MOSS])
 @pytest.mark.parametrize("M,N,K", PINGPONG)
 @pytest.mark.parametrize("fmts", [(E4M3, E4M3), (E5M2, E4M3)])
 def test_gemm_pingpong_ragged_sampled(fq, orc, mode, M, N, K, fmts):
