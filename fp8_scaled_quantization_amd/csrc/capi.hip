@@ -31,6 +31,8 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 // Per-device result of the architecture check (up to 64 devices).
 int g_arch_ok[64];   // 0 unknown, 1 gfx950, -1 other
+// Per-device flag: the GEMM kernels' LDS limits have been set (fp8q_init).
+int g_gemm_prepared[64];
 
 int check_device() {
     int dev = 0;
@@ -54,7 +56,15 @@ extern "C" {
 
 int fp8q_init(void) {
     g_err[0] = 0;
-    return check_device();
+    int rc = check_device();
+    if (rc) return rc;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (!g_gemm_prepared[dev]) {
+        if (fp8q::prepare_gemm_kernels() != 0) return fail(FP8Q_ERR_HIP, "fp8q_init: setting the GEMM kernels' LDS limit failed");
+        g_gemm_prepared[dev] = 1;
+    }
+    return FP8Q_OK;
 }
 
 const char* fp8q_last_error(void) { return g_err; }

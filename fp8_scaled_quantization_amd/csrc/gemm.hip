@@ -387,6 +387,42 @@ static void launch_fmt(const GemmArgs& g, hipStream_t st) {
     else launch_out<MODE, 1, 1>(g, st);
 }
 
+// The dynamic-LDS limit of every GEMM kernel the dispatcher can launch, set once per device by
+// fp8q_init, so that no first launch has to set it (for example inside a stream capture).
+template <class KERN>
+static bool set_lds_limit(KERN kern, size_t bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)bytes) == hipSuccess;
+}
+template <int MODE, int AF, int BF, bool OUT>
+static bool prepare_combo() {
+    bool ok = set_lds_limit(gemm_kernel<MODE, AF, BF, OUT>, kGemmSmem);
+    if constexpr (MODE == kModeBlock) {
+        ok &= set_lds_limit(ppb::gemm_ppb_kernel<MODE, AF, BF, OUT, false, false>, ppb::lds_bytes<MODE>());
+        ok &= set_lds_limit(ppb::gemm_ppb_kernel<MODE, AF, BF, OUT, false, true>, ppb::lds_bytes<MODE>());
+        ok &= set_lds_limit(ppb::gemm_ppb_kernel<MODE, AF, BF, OUT, true, false>, ppb::lds_bytes<MODE>());
+        ok &= set_lds_limit(ppb::gemm_ppb_kernel<MODE, AF, BF, OUT, true, true>, ppb::lds_bytes<MODE>());
+    } else {
+        ok &= set_lds_limit(g2::gemm_kernel<MODE, AF, BF, OUT, 128, 128, 2, 2, 3>, g2::smem_bytes<MODE, 128, 128, 3>());
+        ok &= set_lds_limit(g2::gemm_kernel<MODE, AF, BF, OUT, 64, 64, 2, 2, 2>, g2::smem_bytes<MODE, 64, 64, 2>());
+        ok &= set_lds_limit(ppb::gemm_ppb_kernel<MODE, AF, BF, OUT, false, false>, ppb::lds_bytes<MODE>());
+        ok &= set_lds_limit(pp::gemm_pp_kernel<MODE, AF, BF, OUT>, pp::lds_bytes<MODE>());
+        if constexpr (OUT) ok &= set_lds_limit(pps::gemm_pps_kernel<MODE, AF, BF>, pp::lds_bytes<MODE>());
+    }
+    return ok;
+}
+template <int MODE, int AF, int BF>
+static bool prepare_out() { return prepare_combo<MODE, AF, BF, false>() && prepare_combo<MODE, AF, BF, true>(); }
+template <int MODE>
+static bool prepare_mode() {
+    return prepare_out<MODE, 0, 0>() && prepare_out<MODE, 1, 0>() && prepare_out<MODE, 0, 1>() && prepare_out<MODE, 1, 1>();
+}
+int prepare_gemm_kernels() {
+    const bool ok = prepare_mode<kModeTensor>() && prepare_mode<kModeBlock>() && prepare_mode<kModeMX>() &&
+                    prepare_mode<kModeMoss>();
+    return ok ? 0 : -1;
+}
+
 int launch_gemm(const GemmArgs& g, hipStream_t st) {
     if (g.M == 0 || g.N == 0) return 0;
     switch (g.mode) {

@@ -65,6 +65,8 @@ struct GemmArgs {
     int64_t ldc;
 };
 int launch_gemm(const GemmArgs& g, hipStream_t st);
+// Sets the dynamic-LDS limit of every GEMM kernel on the current device (0 on success).
+int prepare_gemm_kernels();
 
 // Small state kernels and block dequantization (next.hip).
 int launch_history_merge(float* hist_dst, const float* hist_src, int64_t len, float* scale_dst,

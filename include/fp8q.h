@@ -68,8 +68,11 @@ typedef enum {
     FP8Q_BLOCK_E8M0 = 4 /* one power-of-two (UE8M0 byte) scale per (block_r x block_c) block */
 } fp8q_mode;
 
-/* Checks that the current device is gfx950.  Called implicitly by every entry point; returns
- * FP8Q_ERR_NO_DEVICE otherwise. */
+/* Checks that the current device is gfx950 (FP8Q_ERR_NO_DEVICE otherwise) and, once per device,
+ * sets the launch attributes of every GEMM kernel on it (FP8Q_ERR_HIP if that fails).  Every entry
+ * point checks the device by itself, and a GEMM sets its kernel's attributes at its first launch;
+ * calling fp8q_init on each device first means no later call does either, which a caller that
+ * captures library calls into a HIP graph should arrange. */
 int fp8q_init(void);
 
 /* Message describing the calling thread's last non-OK status ("" if none). */

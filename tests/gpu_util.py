@@ -26,6 +26,19 @@ from fp8_scaled_quantization_amd import workloads
 
 DEV = "cuda:0"
 
+_MOSS_ORACLE = {}
+
+
+def moss_oracle_copies(orc, key: str, x: np.ndarray, fmt: int):
+    """The oracle's two MOSS copies of a full workload tensor (groups along its rows, and along its
+    columns), cached for the tests that compare both the single and the dual cast against them:
+    (q, e, qt, et, S)."""
+    if key not in _MOSS_ORACLE:
+        oq, oe, oS = orc.quantize_moss(x, fmt)
+        oqt, oet = orc.quantize_moss_given(x, fmt, oS, transpose=True)
+        _MOSS_ORACLE[key] = (oq, oe, oqt, oet, oS)
+    return _MOSS_ORACLE[key]
+
 
 def to_dev_bf16(bits: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 from fp8_scaled_quantization_amd import workloads
-from tests.gpu_util import DEV, host, same, to_dev
+from tests.gpu_util import DEV, host, moss_oracle_copies, same, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -119,15 +119,14 @@ def test_block_full_size(fq, orc):
     assert same(host(qx), oqx) and same(host(qw), oqw)
 
 
-# ------------------------------------------------------------------ MX, sampled rows at full size
-def test_mx_full_size_sampled(fq, orc):
+# ------------------------------------------------------------------ MX at full size
+def test_mx_full_size(fq, orc):
+    """Both 8192 x 8192 MXFP8 operands, every byte and every E8M0 exponent."""
     A, B = workloads.mx_inputs()
-    rng = np.random.default_rng(44)
-    for x in (A, B):
+    for name, x in (("A", A), ("B", B)):
         q, e, _, _ = fq.quantize(to_dev(x), MX, E4M3)
-        rows = np.unique(np.concatenate([rng.integers(0, x.shape[0], 384), [0, x.shape[0] - 1]]))
-        oq, oe = orc.quantize_mx(np.ascontiguousarray(x[rows]), E4M3)
-        assert same(host(q)[rows], oq) and same(host(e)[rows], oe)
+        oq, oe = orc.quantize_mx(x, E4M3)
+        assert same(host(e), oe, name + " e") and same(host(q), oq, name + " q")
 
 
 def test_mx_past_2g_elements(fq, orc):
@@ -150,20 +149,17 @@ def test_mx_past_2g_elements(fq, orc):
 
 # ------------------------------------------------------------------ MOSS, six copies at full size
 def test_moss_full_size_six_copies(fq, orc):
+    """X, W (E4M3) and dY (E5M2) of the MOSS workload, each in both copies (groups along its rows
+    and, transposed, along its columns with the same S): every byte and exponent, S and amax."""
     X, W, dY = workloads.moss_inputs()
-    rng = np.random.default_rng(55)
-    for x, fmt in ((X, E4M3), (W, E4M3), (dY, E5M2)):
+    for name, x, fmt in (("X", X, E4M3), ("W", W, E4M3), ("dY", dY, E5M2)):
         xd = to_dev(x)
         q, e, S, am = fq.quantize(xd, MOSS, fmt)
         qt, et, _, _ = fq.quantize(xd, MOSS, fmt, transpose_out=True, tensor_scale=S, scale_is_input=True)
-        oS = orc.compute_scale(orc.amax(x), fmt, 1.0)
+        oq, oe, oqt, oet, oS = moss_oracle_copies(orc, name, x, fmt)
         assert _f32(S) == oS and _f32(am) == orc.amax(x)
-        rows = np.unique(np.concatenate([rng.integers(0, x.shape[0], 256), [0, x.shape[0] - 1]]))
-        oq, oe = orc.quantize_moss_given(np.ascontiguousarray(x[rows]), fmt, oS)
-        assert same(host(q)[rows], oq) and same(host(e)[rows], oe)
-        cols = np.unique(np.concatenate([rng.integers(0, x.shape[1], 256), [0, x.shape[1] - 1]]))
-        oqt, oet = orc.quantize_moss_given(np.ascontiguousarray(x[:, cols]), fmt, oS, transpose=True)
-        assert same(host(qt)[cols], oqt) and same(host(et)[cols], oet)
+        assert same(host(e), oe, name + " e") and same(host(q), oq, name + " q")
+        assert same(host(et), oet, name + " et") and same(host(qt), oqt, name + " qt")
 
 
 # ------------------------------------------------------------------ every scheme, small shapes

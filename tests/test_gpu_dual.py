@@ -7,7 +7,7 @@ import pytest
 import torch
 
 from fp8_scaled_quantization_amd import workloads
-from tests.gpu_util import DEV, host, same, to_dev
+from tests.gpu_util import DEV, host, moss_oracle_copies, same, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -97,21 +97,16 @@ def test_dual_given_scale_fused_amax_and_specials(fq, orc, fmt):
         assert same(host(e), oe) and same(host(q), oq) and same(host(et), oet) and same(host(qt), oqt)
 
 
-def test_dual_moss_full_size_sampled(fq, orc):
-    """The MOSS forward/backward operands at full size: S and amax exact, sampled rows of the
-    row-grouped copy and sampled columns (rows of the transposed copy) against the oracle."""
+def test_dual_moss_full_size(fq, orc):
+    """The MOSS forward/backward operands at full size through the one-pass dual cast: S and amax
+    exact, every byte and exponent of both copies against the oracle."""
     X, W, dY = workloads.moss_inputs()
-    rng = np.random.default_rng(56)
-    for x, fmt in ((X, E4M3), (W, E4M3), (dY, E5M2)):
+    for name, x, fmt in (("X", X, E4M3), ("W", W, E4M3), ("dY", dY, E5M2)):
         q, e, qt, et, S, am = fq.quantize_dual(to_dev(x), MOSS, fmt)
-        oS = orc.compute_scale(orc.amax(x), fmt, 1.0)
+        oq, oe, oqt, oet, oS = moss_oracle_copies(orc, name, x, fmt)
         assert _f32(S) == oS and _f32(am) == orc.amax(x)
-        rows = np.unique(np.concatenate([rng.integers(0, x.shape[0], 256), [0, 127, 128, x.shape[0] - 1]]))
-        oq, oe = orc.quantize_moss_given(np.ascontiguousarray(x[rows]), fmt, oS)
-        assert same(host(q)[rows], oq) and same(host(e)[rows], oe)
-        cols = np.unique(np.concatenate([rng.integers(0, x.shape[1], 256), [0, 63, 64, x.shape[1] - 1]]))
-        oqt, oet = orc.quantize_moss_given(np.ascontiguousarray(x[:, cols]), fmt, oS, transpose=True)
-        assert same(host(qt)[cols], oqt) and same(host(et)[cols], oet)
+        assert same(host(e), oe, name + " e") and same(host(q), oq, name + " q")
+        assert same(host(et), oet, name + " et") and same(host(qt), oqt, name + " qt")
 
 
 def test_dual_empty(fq):
