@@ -528,12 +528,50 @@ __global__ __launch_bounds__(NT) void cast_block128_kernel(CastArgs a) {
     const int64_t r0 = br * 128 + (t >> 4), c = bc * 128 + (t & 15) * 8;
     const size_t esz = BF16 ? 2 : 4;
     const char* src = static_cast<const char*>(a.x) + (r0 * a.ld + c) * esz;
-    float v[8 * RPT];
+    // bf16 input stays packed (two values per word) until its cast, which halves the registers the
+    // block takes and lets every workgroup of a 2048 x 7168 weight be resident at once
+    constexpr int VW = BF16 ? 4 : 8;              // registers per 8 values
+    uint32_t raw[VW * RPT];
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) load8<BF16>(src + (int64_t)j * (NT / 16) * a.ld * esz, v + 8 * j);
+    for (int j = 0; j < RPT; ++j) {
+        const uint4* p = reinterpret_cast<const uint4*>(src + (int64_t)j * (NT / 16) * a.ld * esz);
+        const uint4 q0 = p[0];
+        raw[VW * j] = q0.x;
+        raw[VW * j + 1] = q0.y;
+        raw[VW * j + 2] = q0.z;
+        raw[VW * j + 3] = q0.w;
+        if (!BF16) {
+            const uint4 q1 = p[1];
+            raw[VW * j + 4] = q1.x;
+            raw[VW * j + 5] = q1.y;
+            raw[VW * j + 6] = q1.z;
+            raw[VW * j + 7] = q1.w;
+        }
+    }
+    // the 8 values of row slot j as fp32
+    auto unpack = [&](int j, float* v8) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (BF16) {
+                v8[2 * q] = bf16lo(raw[VW * j + q]);
+                v8[2 * q + 1] = bf16hi(raw[VW * j + q]);
+            } else {
+                v8[2 * q] = __uint_as_float(raw[VW * j + 2 * q]);
+                v8[2 * q + 1] = __uint_as_float(raw[VW * j + 2 * q + 1]);
+            }
+        }
+    };
     uint32_t mj[RPT];
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) mj[j] = chunk_max<8>(v + 8 * j);
+    for (int j = 0; j < RPT; ++j) {
+        if (BF16) {
+            mj[j] = bf16w_absmax<4>(raw + VW * j);
+        } else {
+            float v8[8];
+            unpack(j, v8);
+            mj[j] = chunk_max<8>(v8);
+        }
+    }
     uint32_t m = 0;
 #pragma unroll
     for (int j = 0; j < RPT; ++j) m = max(m, mj[j]);
@@ -549,15 +587,23 @@ __global__ __launch_bounds__(NT) void cast_block128_kernel(CastArgs a) {
         // power-of-two block scale: the MX exponent rule over the whole block, exact scaling
         const int e = mx_exponent<FMT>(__uint_as_float(bm));
 #pragma unroll
-        for (int j = 0; j < RPT; ++j) cast_mx<FMT, 8>(v + 8 * j, -e, mj[j] > 0x7F800000u, out + 2 * j);
+        for (int j = 0; j < RPT; ++j) {
+            float v8[8];
+            unpack(j, v8);
+            cast_mx<FMT, 8>(v8, -e, mj[j] > 0x7F800000u, out + 2 * j);
+        }
         if (t == 0) reinterpret_cast<uint8_t*>(a.scales)[br * (a.cols / 128) + bc] = (uint8_t)(e + 127);
     } else {
         const float s = scale_from_amax<FMT>(__uint_as_float(bm), 1.0f);
         const float y = recip_rn(s);
         const bool sok = divisor_ok(s);
 #pragma unroll
-        for (int j = 0; j < RPT; ++j)
-            cast_div<FMT, false, 8>(v + 8 * j, s, y, 0, sok && dividends_ok(mj[j], chunk_min_m1<8>(v + 8 * j)), out + 2 * j);
+        for (int j = 0; j < RPT; ++j) {
+            float v8[8];
+            unpack(j, v8);
+            const uint32_t mn = BF16 ? bf16w_minm1<4>(raw + VW * j) : chunk_min_m1<8>(v8);
+            cast_div<FMT, false, 8>(v8, s, y, 0, sok && dividends_ok(mj[j], mn), out + 2 * j);
+        }
         if (t == 0) reinterpret_cast<float*>(a.scales)[br * (a.cols / 128) + bc] = s;
     }
     uint8_t* dst = a.q + r0 * a.ldq + c;
