@@ -65,6 +65,7 @@ def parse():
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                             "gemm_moss_16384x4096x4096_hbm_traffic.md")
 GEMM_SOURCES = ("fp8_scaled_quantization_amd/csrc/gemm_pp.cuh", "fp8_scaled_quantization_amd/csrc/gemm_ppb.cuh",
+                "fp8_scaled_quantization_amd/csrc/gemm_pps.cuh",
                 "fp8_scaled_quantization_amd/csrc/gemm_kernel.cuh",
                 "fp8_scaled_quantization_amd/csrc/gemm.hip", "fp8_scaled_quantization_amd/csrc/kernels.h",
                 "fp8_scaled_quantization_amd/csrc/common.cuh")

@@ -55,9 +55,9 @@ constexpr size_t lds_bytes() { return (size_t)kScBase + 2 * (size_t)quad_rows<MO
 // The data of step ks goes into the stage of step s (ks = s except past the last step, where the
 // copies repeat the last step's data into a stage no step reads, which keeps the loop free of
 // branches).
-__device__ __forceinline__ void copy_one(uint8_t* smem, int s, int ks, int g, int wi, int j, rsrc_t ra, rsrc_t rb,
+__device__ __forceinline__ void copy_one(uint32_t sbase, int s, int ks, int g, int wi, int j, rsrc_t ra, rsrc_t rb,
                                          uint32_t voffA, uint32_t voffB, uint32_t lda, uint32_t ldb) {
-    uint8_t* st = smem + (s % STAGES) * kStage;
+    const uint32_t st = sbase + (uint32_t)((s % STAGES) * kStage);
     const uint32_t koff = (uint32_t)ks * BK;
     if (j < 4) {
         const uint32_t r0 = (uint32_t)(128 * g + 32 * wi + 8 * j);
@@ -73,8 +73,8 @@ __device__ __forceinline__ void copy_one(uint8_t* smem, int s, int ks, int g, in
 // range-checked lane offset: the last quad of a row may end past the row (K steps not a multiple of
 // 4), and past the array's end on its last row, where the buffer range turns the excess into zeros.
 template <int MODE>
-__device__ __forceinline__ void copy_quad(uint8_t* smem, int s, int r0, rsrc_t rs, uint32_t voffS, uint32_t sc_row) {
-    uint8_t* sq = smem + kScBase + ((s >> 2) & 1) * (quad_rows<MODE>() * 16);
+__device__ __forceinline__ void copy_quad(uint32_t sbase, int s, int r0, rsrc_t rs, uint32_t voffS, uint32_t sc_row) {
+    const uint32_t sq = sbase + (uint32_t)(kScBase + ((s >> 2) & 1) * (quad_rows<MODE>() * 16));
     const uint32_t first = (uint32_t)(r0 < BM ? r0 : r0 - BM);
     copy8(sq + r0 * 16, rs, voffS + (uint32_t)s * 4, first * sc_row, 0u);
 }
@@ -87,11 +87,11 @@ __device__ __forceinline__ int wave_quads(int g, int wi) {
     return (MODE != kModeBlock && wi < 2) ? 1 : 0;
 }
 template <int MODE>
-__device__ __forceinline__ void issue_quad(uint8_t* smem, int s, int g, int wi, rsrc_t rsa, rsrc_t rsb, uint32_t voffS,
+__device__ __forceinline__ void issue_quad(uint32_t sbase, int s, int g, int wi, rsrc_t rsa, rsrc_t rsb, uint32_t voffS,
                                            uint32_t sc_row) {
     if (MODE == kModeTensor) return;
-    if (g == 1) copy_quad<MODE>(smem, s, 64 * wi, rsa, voffS, sc_row);
-    else if (MODE != kModeBlock && wi < 2) copy_quad<MODE>(smem, s, BM + 64 * wi, rsb, voffS, sc_row);
+    if (g == 1) copy_quad<MODE>(sbase, s, 64 * wi, rsa, voffS, sc_row);
+    else if (MODE != kModeBlock && wi < 2) copy_quad<MODE>(sbase, s, BM + 64 * wi, rsb, voffS, sc_row);
 }
 
 // Raw 32-bit word holding a weight-block scale, through the scalar cache: the fp32 scale itself, or
@@ -123,6 +123,7 @@ __global__ __launch_bounds__(512, 1) void gemm_ppb_kernel(GemmArgs g) {
     constexpr bool RSC = BLOCKED && !AST;          // per-row activation scales in the quads
     constexpr int QB = quad_rows<MODE>() * 16;     // bytes of one scale quad
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const uint32_t sbase = g2::lds_addr(smem);    // LDS address of the dynamic allocation (copy targets)
 
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -182,11 +183,11 @@ __global__ __launch_bounds__(512, 1) void gemm_ppb_kernel(GemmArgs g) {
 
     // ---- prologue: both halves of steps 0 and 1, the first scale quad
 #pragma unroll
-    for (int j = 0; j < 6; ++j) copy_one(smem, 0, 0, grp, wi, j, ra, rb, voffA, voffB, ulda, uldb);
-    if (!(BLOCKED && AST)) issue_quad<MODE>(smem, 0, grp, wi, rsa, rsb, voffS, sc_row);
+    for (int j = 0; j < 6; ++j) copy_one(sbase, 0, 0, grp, wi, j, ra, rb, voffA, voffB, ulda, uldb);
+    if (!(BLOCKED && AST)) issue_quad<MODE>(sbase, 0, grp, wi, rsa, rsb, voffS, sc_row);
     if (nk > 1) {
 #pragma unroll
-        for (int j = 0; j < 6; ++j) copy_one(smem, 1, 1, grp, wi, j, ra, rb, voffA, voffB, ulda, uldb);
+        for (int j = 0; j < 6; ++j) copy_one(sbase, 1, 1, grp, wi, j, ra, rb, voffA, voffB, ulda, uldb);
         wait_vm<6>();
     } else {
         wait_vm0();
@@ -226,11 +227,11 @@ __global__ __launch_bounds__(512, 1) void gemm_ppb_kernel(GemmArgs g) {
         v8i fa[4], fb[4];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            if (q < 6) copy_one(smem, k + 2, min(k + 2, nk - 1), grp, wi, q, ra, rb, voffA, voffB, ulda, uldb);
+            if (q < 6) copy_one(sbase, k + 2, min(k + 2, nk - 1), grp, wi, q, ra, rb, voffA, voffB, ulda, uldb);
             if (q < 4) fa[q] = frag(sa + rowA + q * 16 * BK, cLo, cHi);
             else fb[q - 4] = frag(sb + rowB + (q - 4) * 16 * BK, cLo, cHi);
         }
-        if (quad) issue_quad<MODE>(smem, k + 2, grp, wi, rsa, rsb, voffS, sc_row);
+        if (quad) issue_quad<MODE>(sbase, k + 2, grp, wi, rsa, rsb, voffS, sc_row);
         // BLOCK: the block-scale products of this step, fl(sx * sw)
         float rs[16];
         if (BLOCKED) {
