@@ -347,6 +347,16 @@ static void launch_pp(const GemmArgs& g, hipStream_t st) {
 
 static bool fits_u32(int64_t bytes) { return bytes >= 0 && bytes < ((int64_t)1 << 32); }
 
+// LDS stages of the pipelined kernel's tiles.  128 x 128 TENSOR tiles keep one more step's loads in
+// flight (4 x 32 KiB; 2048 x 2048 x 4096 measured 30.3-31.1 us against 31.7-32.0 us with 3 stages);
+// MX/MOSS keep the scale-quad schedule of 3 stages.  The 64 x 64 tiles keep 2 stages: at
+// 1024 x 1024 x 2048 their 256 workgroups pull 64 MiB through L2 in ~9 us, and 6 stages made the
+// call slower (10.2 us against 8.6 us per call in a replayed graph).
+template <int MODE>
+constexpr int small_stages() { return 2; }
+template <int MODE>
+constexpr int mid_stages() { return MODE == kModeTensor ? 4 : 3; }
+
 template <int MODE, int AFMT, int BFMT, bool OUT>
 static void launch_sel(const GemmArgs& g, hipStream_t st) {
     const bool fast = g.K > 0 && g.K % 128 == 0 && fits_u32(g.M * g.lda) && fits_u32(g.N * g.ldb) &&
@@ -368,8 +378,8 @@ static void launch_sel(const GemmArgs& g, hipStream_t st) {
         const int64_t small_tiles = ((g.M + 127) / 128) * ((g.N + 127) / 128);
         if (big_tiles >= 192) launch_pp<MODE, AFMT, BFMT, OUT>(g, st);
         else if (mid_tiles >= 192) launch_ppb<MODE, AFMT, BFMT, OUT>(g, st);
-        else if (small_tiles >= 256) launch_v2<MODE, AFMT, BFMT, OUT, 128, 128, 2, 2, 3>(g, st);
-        else launch_v2<MODE, AFMT, BFMT, OUT, 64, 64, 2, 2, 2>(g, st);
+        else if (small_tiles >= 256) launch_v2<MODE, AFMT, BFMT, OUT, 128, 128, 2, 2, mid_stages<MODE>()>(g, st);
+        else launch_v2<MODE, AFMT, BFMT, OUT, 64, 64, 2, 2, small_stages<MODE>()>(g, st);
     }
 }
 
@@ -403,8 +413,10 @@ static bool prepare_combo() {
         ok &= set_lds_limit(ppb::gemm_ppb_kernel<MODE, AF, BF, OUT, true, false>, ppb::lds_bytes<MODE>());
         ok &= set_lds_limit(ppb::gemm_ppb_kernel<MODE, AF, BF, OUT, true, true>, ppb::lds_bytes<MODE>());
     } else {
-        ok &= set_lds_limit(g2::gemm_kernel<MODE, AF, BF, OUT, 128, 128, 2, 2, 3>, g2::smem_bytes<MODE, 128, 128, 3>());
-        ok &= set_lds_limit(g2::gemm_kernel<MODE, AF, BF, OUT, 64, 64, 2, 2, 2>, g2::smem_bytes<MODE, 64, 64, 2>());
+        ok &= set_lds_limit(g2::gemm_kernel<MODE, AF, BF, OUT, 128, 128, 2, 2, mid_stages<MODE>()>,
+                            g2::smem_bytes<MODE, 128, 128, mid_stages<MODE>()>());
+        ok &= set_lds_limit(g2::gemm_kernel<MODE, AF, BF, OUT, 64, 64, 2, 2, small_stages<MODE>()>,
+                            g2::smem_bytes<MODE, 64, 64, small_stages<MODE>()>());
         ok &= set_lds_limit(ppb::gemm_ppb_kernel<MODE, AF, BF, OUT, false, false>, ppb::lds_bytes<MODE>());
         ok &= set_lds_limit(pp::gemm_pp_kernel<MODE, AF, BF, OUT>, pp::lds_bytes<MODE>());
         if constexpr (OUT) ok &= set_lds_limit(pps::gemm_pps_kernel<MODE, AF, BF>, pp::lds_bytes<MODE>());

@@ -108,6 +108,21 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Wait until at most r * PER vector-memory operations of this wave are outstanding, for a
+// wave-uniform r in 0 .. R (the count must be an immediate, so each r has its own wait).
+template <int PER, int R>
+__device__ __forceinline__ void wait_steps(int r) {
+    if constexpr (R == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (r >= R) {
+            wait_vmcnt<R * PER>();
+            return;
+        }
+        wait_steps<PER, R - 1>(r);
+    }
+}
+
 template <int MODE, int BM, int BN, int STAGES>
 struct Layout {
     static constexpr bool SCALED = MODE == kModeMX || MODE == kModeMoss;
@@ -167,8 +182,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmArgs g
     static_assert(L::kScRows % 64 == 0, "scale rows per wave instruction");
     constexpr int LD_LO = A_LD + B_LD;                           // per stage without scales
     constexpr int SC_LO = SC_LD_TOTAL / NW;                      // scale instructions of every wave
-    static_assert(STAGES >= 2 && STAGES <= 3, "stage count");
-    static_assert(LD_LO + SC_LO + 1 < 64, "vmcnt range");
+    // TENSOR takes deeper rings (no scale quads, so every step carries the same instruction count)
+    static_assert(STAGES >= 2 && STAGES <= (SCALED ? 3 : 8), "stage count");
+    static_assert(LD_LO + SC_LO + 1 < 64 && LD_LO * (STAGES - 2) < 64, "vmcnt range");
 
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -249,7 +265,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmArgs g
 
     for (int64_t kt = 0; kt < nk; ++kt) {
         // step kt has landed once only the later steps' loads (at most STAGES-2 of them) remain
-        if (STAGES == 3 && kt + 1 < nk) {
+        if (!SCALED) {
+            wait_steps<LD_LO, STAGES - 2>((int)min((int64_t)(STAGES - 2), nk - 1 - kt));
+        } else if (STAGES == 3 && kt + 1 < nk) {
             // one later step in flight: its instruction count depends on whether it carries scales
             if (L::kScRows > 0 && (kt + 1) % SQ == 0) {
                 if (extra_sc) wait_vmcnt<LD_LO + SC_LO + 1>();
