@@ -350,7 +350,9 @@ def measure_casts_cold_warm(torch, fq, o, w2, w3, w4, w5, reps=10):
     last-level cache, so the input comes from HBM and no earlier writes are pending.  Warm: the
     same launch repeated back to back, so an input that fits the last-level cache is served from
     it.  GB/s counts the algorithmic bytes (input read, plus the amax pass's read where the scale
-    is derived, FP8 and scale bytes written)."""
+    is derived, FP8 and scale bytes written).  A plain device copy (256 MiB read, 256 MiB written,
+    torch's elementwise kernel) is timed the same way as the reference for what HBM delivers to a
+    streaming kernel, and each cast's cold rate is also given as a fraction of the copy's."""
     dev = "cuda:0"
     E4M3, E5M2 = fq.E4M3, fq.E5M2
     TENSOR, BLOCK, MX, MOSS = fq.TENSOR, fq.BLOCK, fq.MX, fq.MOSS
@@ -369,6 +371,9 @@ def measure_casts_cold_warm(torch, fq, o, w2, w3, w4, w5, reps=10):
             lambda: QD(MOSS, E4M3, w5["X"], o["q5X"], o["e5X"], o["q5XT"], o["e5XT"], o["S5X"], False, o["m5X"]),
             16384 * 4096 * 6 + 2 * 16384 * 128),
     }
+    csrc = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    cdst = torch.empty_like(csrc)
+    casts["device copy 256 MiB (reference)"] = (lambda: torch.neg(csrc, out=cdst), 2 * csrc.numel() * 4)
     out = {}
     for name, (fn, nbytes) in casts.items():
         fn()
@@ -394,7 +399,10 @@ def measure_casts_cold_warm(torch, fq, o, w2, w3, w4, w5, reps=10):
         out[name] = {"cold_ms": round(cold_ms, 5), "cold_gbs": round(nbytes / (cold_ms * 1e-3) / 1e9, 1),
                      "cold_pct_hbm_peak": round(100 * nbytes / (cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
                      "warm_ms": round(warm_ms, 5), "warm_gbs": round(nbytes / (warm_ms * 1e-3) / 1e9, 1)}
-    del flush
+    del flush, csrc, cdst
+    copy = out["device copy 256 MiB (reference)"]["cold_gbs"]
+    for v in out.values():
+        v["cold_pct_of_copy"] = round(100 * v["cold_gbs"] / copy, 1)
     return out
 
 
