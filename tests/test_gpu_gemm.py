@@ -220,6 +220,27 @@ def test_gemm_stream_full(fq, orc, mode, M, N, K):
 
 
 @pytest.mark.parametrize("mode", [TENSOR, MX, MOSS])
+@pytest.mark.parametrize("M,N,K,fmts", [(2048, 2048, 128, (E4M3, E4M3)), (2000, 2100, 384, (E4M3, E4M3)),
+                                        (2048, 2048, 1152, (E5M2, E4M3))])
+def test_gemm_pipelined_mid_tiles_full(fq, orc, mode, M, N, K, fmts):
+    """Every output of problems run by the pipelined kernel's 128 x 128 tiles (at least 256 of them,
+    fewer than 192 of 256 x 128): in TENSOR mode its ring has 4 stages and the wait before a K step
+    lets the next min(2, steps left) steps' loads stay in flight, so 1, 3 and 9 K steps cover every
+    count; MX/MOSS take the 3-stage scale-quad schedule.  2000 x 2100 has partial tiles in M and N."""
+    afmt, bfmt = fmts
+    xa = workloads.random_matrix(M + 13 * K, M, K, 2.0)
+    xb = workloads.random_matrix(N + 17 * K, N, K, 0.05)
+    A, (hqa, hsa, hga) = _quant_operand(fq, orc, xa, mode, afmt, None)
+    B, (hqb, hsb, hgb) = _quant_operand(fq, orc, xb, mode, bfmt, None)
+    Ad = _deq(orc, mode, hqa, hsa, hga, afmt, (1, 128))
+    Bd = _deq(orc, mode, hqb, hsb, hgb, bfmt, (1, 128))
+    Cref, D, E, Sg = reference_terms(orc, Ad, Bd)
+    C32 = host(_run(fq, mode, A, afmt, B, bfmt, OUT_F32))
+    Cbf = host(_run(fq, mode, A, afmt, B, bfmt, OUT_BF16))
+    check_gemm(C32, Cbf, Cref, D, E, K, "pipelined 128x128 mode %d %dx%dx%d" % (mode, M, N, K), Sg)
+
+
+@pytest.mark.parametrize("mode", [TENSOR, MX, MOSS])
 @pytest.mark.parametrize("M,N,K", PINGPONG)
 @pytest.mark.parametrize("fmts", [(E4M3, E4M3), (E5M2, E4M3)])
 def test_gemm_pingpong_ragged_sampled(fq, orc, mode, M, N, K, fmts):
