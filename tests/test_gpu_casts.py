@@ -34,13 +34,16 @@ def test_amax(fq, orc, shape, bf16):
     assert _f32(out) == orc.amax(x)
 
 
-def test_amax_strided_nan_empty(fq, orc):
-    x = workloads.random_matrix(7, 64, 96, 1.0, bf16=False)
-    xd = to_dev(x)[:, :64]                      # ld = 96 > cols = 64
+@pytest.mark.parametrize("bf16", [False, True])
+def test_amax_strided_nan_empty(fq, orc, bf16):
+    x = workloads.random_matrix(7, 64, 96, 1.0, bf16=bf16)
+    xd = to_dev(x)[:, :64]                      # ld = 96 > cols = 64: the row-strided kernel
     out = torch.zeros(1, dtype=torch.float32, device=DEV)
     fq.fp8_amax(xd, out)
     assert _f32(out) == orc.amax(np.ascontiguousarray(x[:, :64]))
-    x[3, 5] = np.nan
+    x[3, 5] = np.uint16(0x7FC0) if bf16 else np.nan
+    fq.fp8_amax(to_dev(x)[:, :64], out)
+    assert np.isnan(_f32(out))
     fq.fp8_amax(to_dev(x), out)
     assert np.isnan(_f32(out))
     fq.fp8_amax(torch.zeros((0, 64), dtype=torch.float32, device=DEV), out)

@@ -242,7 +242,7 @@ def test_gemm_pipelined_mid_tiles_full(fq, orc, mode, M, N, K, fmts):
 
 @pytest.mark.parametrize("mode", [TENSOR, MX, MOSS])
 @pytest.mark.parametrize("M,N,K", PINGPONG)
-@pytest.mark.parametrize("fmts", [(E4M3, E4M3), (E5M2, E4M3)])
+@pytest.mark.parametrize("fmts", [(E4M3, E4M3), (E5M2, E4M3), (E4M3, E5M2)])
 def test_gemm_pingpong_ragged_sampled(fq, orc, mode, M, N, K, fmts):
     afmt, bfmt = fmts
     xa = workloads.random_matrix(M + 7 * K, M, K, 2.0)
