@@ -13,7 +13,9 @@ After the timed steps, the next-step paths are timed on the same inputs (reporte
 "next_rows", not part of the headline): automatic weight scaling against a just-in-time max
 reduction of W, the delayed-scaling history merge, UE8M0 128x128 weight quantization and block
 dequantization, and the block GEMM with UE8M0 weight scales and with a static activation scale.
-Each cast is also timed alone, cold (input from HBM) and warm ("quantize_cold_warm").
+Each cast is also timed alone, cold (input from HBM) and warm ("quantize_cold_warm"), beside a
+plain 256 MiB device copy timed the same way as the reference for what HBM delivers to a streaming
+kernel.
 The headline value is the step's total GEMM flops (2 M N K per GEMM) divided by the step time,
 i.e. scaled-GEMM TFLOP/s including every quantization the path performs.  "per_config" gives each
 workload's GEMM flops over the summed time of all its launches beside the ceiling the two
