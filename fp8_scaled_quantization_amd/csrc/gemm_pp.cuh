@@ -278,16 +278,14 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
     lane_offsets(m0, n0);
 
     // ---- a tile's pipeline fill: group 1 sends A and B0 of step 0 and A of step 1; group 0 sends
-    // B1 of step 0 and B0 of step 1 (afterwards it sends B1 of step k+1 in its memory phase for step
-    // k and B0 of step k+2 after its MFMAs for step k; group 1 sends A of step k+2 in its memory
-    // phase).  For every tile but the first it goes out before the previous tile's epilogue, whose
-    // stores then follow it in the wave's vector-memory queue.
+    // B1 of step 0 (afterwards it sends B0 and B1 of step k+1 in its memory phase for step k; group
+    // 1 sends A of step k+2 in its memory phase).  For every tile but the first it goes out before
+    // the previous tile's epilogue, whose stores then follow it in the wave's vector-memory queue.
     const int k1 = min(nk - 1, 1);   // (nk >= 1; a scalar min, not a select the compiler would keep in a VGPR)
     auto fill = [&]() {
         const uint32_t la = fresh(ulda), lb = fresh(uldb), ls = fresh(usc), sb0 = fresh(sbase);
         if (grp == 0) {
             copy_B(sb0, 0, 0, 128, wi, rb, voffB, lb);
-            copy_B(sb0, 1, k1, 0, wi, rb, voffB, lb);
         } else {
             copy_A(sb0, 0, 0, wi, ra, voffA, la);
             copy_B(sb0, 0, 0, 0, wi, rb, voffB, lb);
@@ -309,10 +307,9 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
         uint32_t m0n = 0, n0n = 0;
         if (tile_n < ntiles) coords(tile_n, m0n, n0n);
 
-        if (grp == 0) {
-            if (behind) wait_vm<4 + kStores>();
-            else wait_vm<4>();
-        } else {
+        // group 1's A and B0 of step 0 (and the scale quad) land before the barrier; group 0's
+        // fill (B1 of step 0) is waited for in its first memory phase
+        if (grp == 1) {
             if (behind) wait_vm<8 + kStores>();
             else wait_vm<8>();
         }
@@ -350,13 +347,19 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
                 const uint8_t* sa = smem + (k & 1) * kStage;
                 const uint8_t* sb = sa + kA;
                 if (grp == 0) {
-                    // A and B0 of step k; B1 of step k+1 (4 copies), one per three fragment reads
+                    // A and B0 of step k; B0, then B1, of step k+1 (8 copies, one per fragment
+                    // read; that stage's B0 was last read in the previous memory phase, its B1 one
+                    // phase earlier)
                     const uint32_t st = sk1 + kA;
                     const uint32_t koff = (uint32_t)min(k + 1, nk - 1) * BK;
-                    uint32_t l = st + (uint32_t)(128 + wi * 32) * BK, ro = (uint32_t)(128 + wi * 32) * uldb;
+                    uint32_t l = st + (uint32_t)(wi * 32) * BK, ro = (uint32_t)(wi * 32) * uldb;
 #pragma unroll
                     for (int q = 0; q < 12; ++q) {
-                        if (q % 3 == 0) {
+                        if (q < 8) {
+                            if (q == 4) {
+                                l = st + (uint32_t)(128 + wi * 32) * BK;
+                                ro = (uint32_t)(128 + wi * 32) * uldb;
+                            }
                             copy8(l, rb, voffB, ro, koff);
                             l = fresh(l + 8 * BK);
                             ro = fresh(ro + 8 * uldb);
@@ -364,9 +367,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
                         if (q < 4) fa[q] = frag(sa + rowA + q * 16 * BK, cLo, cHi);
                         else fb[q - 4] = frag(sb + rowB + (q - 4) * 16 * BK, cLo, cHi);
                     }
-                    // B1 of step k (sent one memory phase ago) lands before group 1 reads it next
-                    // phase; newer: B0 of step k+1 (sent in the last compute phase, or the fill) and
-                    // this phase's B1
+                    // B1 of step k (sent one memory phase ago, or the fill) lands before group 1
+                    // reads it next phase; newer: this phase's 8 copies
                     if (st0) wait_vm<8 + kStores>();
                     else wait_vm<8>();
                 } else {
@@ -439,23 +441,10 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
             for (int i = 0; i < 4; ++i)
                 asm volatile("" ::"v"(acc[i][0]), "v"(acc[i][1]), "v"(acc[i][2]), "v"(acc[i][3]), "v"(acc[i][4]),
                              "v"(acc[i][5]), "v"(acc[i][6]), "v"(acc[i][7]));
-            if (grp == 0) {
-                // B0 of step k+2, into the stage group 0 finished reading last phase, sent after this
-                // phase's MFMAs: group 1's memory phase, which moves A, is the longer one
-                const uint32_t st = sk + kA;
-                const uint32_t koff = (uint32_t)min(k + 2, nk - 1) * BK;
-                uint32_t l = st + (uint32_t)(wi * 32) * BK, ro = (uint32_t)(wi * 32) * uldb;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    copy8(l, rb, voffB, ro, koff);
-                    l = fresh(l + 8 * BK);
-                    ro = fresh(ro + 8 * uldb);
-                }
-                // B0 of step k+1 (sent in the last compute phase, or the fill) lands before group 0
-                // reads it next phase; newer: B1 of step k+1 (this memory phase) and B0 of step k+2
-                if (st0) wait_vm<8 + kStores>();
-                else wait_vm<8>();
-            }
+            // group 0: B0 of step k+1 (sent in the memory phase) lands before group 0 reads it next
+            // phase; newer: the 4 B1 copies sent after it (at a tile's first step the previous
+            // tile's stores are older than these copies and complete first anyway)
+            if (grp == 0) wait_vm<4>();
             barrier();
         }
         if (grp == 0) barrier();          // matches group 1's extra barrier at the start

@@ -132,12 +132,11 @@ __global__ __launch_bounds__(512, 1) void gemm_pps_kernel(GemmArgs g) {
     uint32_t voffB = (uint32_t)(lane >> 3) * uldb + ch + n0 * uldb;
     uint32_t voffS = (uint32_t)lane * usc + (wi < 2 ? m0 : n0) * usc;
 
-    // ---- the stream's start: steps 0 and 1 of the first tile (group 0: B1 of step 0, B0 of step
-    // 1; group 1: A and B0 of step 0, the first scale quad, A of step 1)
+    // ---- the stream's start: group 0 sends B1 of step 0 (it sends B0 and B1 of step k+1 in its
+    // memory phase for step k); group 1 sends A and B0 of step 0, the first scale quad and A of
+    // step 1, and waits for all but A of step 1
     if (grp == 0) {
         pp::copy_B(sbase, 0, 0, 128, wi, rb, voffB, uldb);
-        pp::copy_B(sbase, 1, 1, 0, wi, rb, voffB, uldb);
-        wait_vm<4>();
     } else {
         pp::copy_A(sbase, 0, 0, wi, ra, voffA, ulda);
         pp::copy_B(sbase, 0, 0, 0, wi, rb, voffB, uldb);
@@ -194,16 +193,21 @@ __global__ __launch_bounds__(512, 1) void gemm_pps_kernel(GemmArgs g) {
                 const uint8_t* sa = smem + (k & 1) * kStage;
                 const uint8_t* sb = sa + kA;
                 if (grp == 0) {
-                    // B1 of stream step k+1: this tile's step, or after the last step the next
-                    // tile's step 0 (past the last tile: the last step again, into a stage no step
-                    // reads)
+                    // B0, then B1, of stream step k+1 (8 copies, one per fragment read): this
+                    // tile's step, or after the last step the next tile's step 0 (past the last
+                    // tile: the last step again, into a stage no step reads).  Both regions of that
+                    // stage were last read one and two phases ago.
                     const int s = k + 1;
                     const uint32_t vB = voffB + ((s >= nk && more) ? dB : 0u);
                     const uint32_t koff = (uint32_t)(s < nk ? s : (more ? s - nk : nk - 1)) * BK;
-                    uint32_t l = sk1 + kA + (uint32_t)(128 + wi * 32) * BK, ro = (uint32_t)(128 + wi * 32) * uldb;
+                    uint32_t l = sk1 + kA + (uint32_t)(wi * 32) * BK, ro = (uint32_t)(wi * 32) * uldb;
 #pragma unroll
                     for (int q = 0; q < 12; ++q) {
-                        if (q % 3 == 0) {
+                        if (q < 8) {
+                            if (q == 4) {
+                                l = sk1 + kA + (uint32_t)(128 + wi * 32) * BK;
+                                ro = (uint32_t)(128 + wi * 32) * uldb;
+                            }
                             copy8(l, rb, vB, ro, koff);
                             l = fresh(l + 8 * BK);
                             ro = fresh(ro + 8 * uldb);
@@ -212,7 +216,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pps_kernel(GemmArgs g) {
                         else fb[q - 4] = frag(sb + rowB + (q - 4) * 16 * BK, cLo, cHi);
                     }
                     // B1 of step k (sent one memory phase ago) lands before group 1 reads it next
-                    // phase; newer: B0 of step k+1 (last compute phase) and this phase's B1 copies
+                    // phase; newer: this phase's 8 copies
                     wait_vm_n(8 + st0);
                 } else {
                     // A of stream step k+2, and the scale quad that starts there
@@ -275,22 +279,10 @@ __global__ __launch_bounds__(512, 1) void gemm_pps_kernel(GemmArgs g) {
             for (int i = 0; i < 4; ++i)
                 asm volatile("" ::"v"(acc[i][0]), "v"(acc[i][1]), "v"(acc[i][2]), "v"(acc[i][3]), "v"(acc[i][4]),
                              "v"(acc[i][5]), "v"(acc[i][6]), "v"(acc[i][7]));
-            if (grp == 0) {
-                // B0 of stream step k+2, after this phase's MFMAs
-                const int s = k + 2;
-                const uint32_t vB = voffB + ((s >= nk && more) ? dB : 0u);
-                const uint32_t koff = (uint32_t)(s < nk ? s : (more ? s - nk : nk - 1)) * BK;
-                uint32_t l = sk + kA + (uint32_t)(wi * 32) * BK, ro = (uint32_t)(wi * 32) * uldb;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    copy8(l, rb, vB, ro, koff);
-                    l = fresh(l + 8 * BK);
-                    ro = fresh(ro + 8 * uldb);
-                }
-                // B0 of step k+1 lands before group 0 reads it next phase; newer: this step's B1
-                // copies and the B0 copies just sent
-                wait_vm_n(8 + st0);
-            }
+            // group 0: B0 of stream step k+1 (sent in the memory phase) lands before group 0 reads
+            // it next phase; newer: the 4 B1 copies sent after it (at a tile's first step the last
+            // tile's stores are older than these copies, so they complete first anyway)
+            if (grp == 0) wait_vm<4>();
             barrier();
         }
 
