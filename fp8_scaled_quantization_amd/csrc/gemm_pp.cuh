@@ -19,19 +19,19 @@
 // phase (phase 2k).  Group 1 reads B rows 128-255 (B1) of step k in its memory phase (phase 2k+1)
 // but reads A of step k during its compute phase for step k-1 (also phase 2k), one 16-row A block
 // right after the last MFMA that used the previous step's block, so it needs no extra registers.
-// A and B0 of a stage are therefore free one phase after they are first read, and every copy gets
-// about two phases to land:
-//   A of step k+2 (and the scale quad of a quad's first step)
-//                 group 1, memory phase for step k (phase 2k+1), waited at the end of phase 2k+3;
-//   B0 of step k+2  group 0, after the MFMAs of its compute phase for step k (phase 2k+1), waited at
-//                 the end of phase 2k+3;
-//   B1 of step k+1  group 0, memory phase for step k (phase 2k),   waited at the end of phase 2k+2.
+// A and B0 of a stage are therefore free one phase after they are first read, B1 one phase later:
+//   A of step k+2       group 1, memory phase for step k (phase 2k+1), waited at the end of 2k+3;
+//   scale quad of steps s .. s+3
+//                       group 1, memory phase for step s-2 after its A copies, waited with them;
+//   B0 and B1 of step k+1
+//                       group 0, memory phase for step k (phase 2k); B0 waited at the end of phase
+//                       2k+1, B1 at the end of phase 2k+2.
 // A copy instruction can hold its wave while the address unit is busy, so copies never sit between
-// a wave's MFMAs: group 1 interleaves its eight with its fragment reads, group 0 sends its B1 copies
-// among its fragment reads and its B0 copies after its MFMAs.  (Measured with per-phase timestamps:
-// with all twelve A and B0 copies in group 1's memory phase, that phase took ~1470 cycles against
-// ~1190 for group 0's compute phase, and the matrix core idled for the difference; with the B0
-// copies moved, a K step takes ~3000 cycles instead of ~3150.)
+// a wave's MFMAs: each group interleaves its eight copies with its fragment reads, and group 0's
+// compute phase holds only its MFMAs and one wait.  (Measured with per-phase timestamps on a MOSS
+// 16384x4096x4096 product: with all twelve A and B0 copies in group 1's memory phase a K step took
+// ~3150 cycles; with B0 sent after group 0's MFMAs, ~2790; with both B halves in group 0's memory
+// phase, ~2700, the memory phases (~1150 cycles each) now longer than the compute phases.)
 //
 // Global->LDS copies use buffer_load_dwordx4 ... lds (no VGPR staging; rows past M or N read zero
 // through the buffer range), with each 16-byte chunk c of tile row r stored at chunk position
@@ -193,7 +193,7 @@ __device__ __forceinline__ void copy_B(uint32_t sbase, int s, int ks, int base, 
         ro = fresh(ro + 8 * ldb);
     }
 }
-// Group 0, wave wi, every fourth step: two instructions of the scale quad for steps s .. s+3.
+// Group 1, wave wi, every fourth step: two instructions of the scale quad for steps s .. s+3.
 // The K offset goes into the range-checked lane offset: when the K steps are not a multiple of 4
 // the last quad of a row ends past the row, and on the array's last row past its end, where the
 // buffer range turns the excess into zeros.
