@@ -21,8 +21,8 @@ i.e. scaled-GEMM TFLOP/s including every quantization the path performs.  "per_c
 workload's GEMM flops over the summed time of all its launches beside the ceiling the two
 rooflines allow (GEMM flops at the FP8 MFMA peak plus its cast bytes at the HBM peak).  The
 oracle leg ("cpu_baseline", skipped with --no-cpu-baseline) times the CPU oracle per workload on a
-bounded sample and, outside that timing, reports the quantization SNR ("snr_db") of the MX and
-MOSS operands the timed steps wrote.
+bounded sample and, outside that timing, reports the quantization SNR ("snr_db") of the
+fine-grained, MX and MOSS operands the timed steps wrote.
 
 The timed steps are replays of HIP graphs captured from the same library calls (one graph per
 delayed-scaling step index, since that input changes with the step); --no-graph times eager
@@ -580,12 +580,17 @@ def oracle_leg(h, o, torch):
                            "value = sampled GEMM flops over the summed oracle time")}
 
     # quantization SNR (dB, fp64 over whole tensors) of the operands the GPU step quantized
-    def snr(bits, mode, q, e, fmt, S=None):
-        xhat = orc.dequantize(mode, q.cpu().numpy(), fmt, e.cpu().numpy(), S)
+    def snr(bits, mode, q, e, fmt, S=None, block=(128, 128)):
+        if mode == 1:
+            xhat = orc.dequantize(mode, q.cpu().numpy(), fmt, e.cpu().numpy(), None, block=block)
+        else:
+            xhat = orc.dequantize(mode, q.cpu().numpy(), fmt, e.cpu().numpy(), S)
         return round(orc.snr_db(wl.bf16_bits_to_f32(bits), xhat), 3)
 
     S5 = {n: np.float32(o["S5" + n].item()) for n in ("X", "W", "G")}
-    snr_db = {"MXFP8 A 8192x8192 (MX)": snr(h["A4"], 2, o["q4a"], o["e4a"], 0),
+    snr_db = {"fine-grained X 4096x7168 (1x128, 0.1% x50 outliers)": snr(h["X3"], 1, o["q3x"], o["s3x"], 0, block=(1, 128)),
+              "fine-grained W 2048x7168 (128x128)": snr(h["W3"], 1, o["q3w"], o["s3w"], 0),
+              "MXFP8 A 8192x8192 (MX)": snr(h["A4"], 2, o["q4a"], o["e4a"], 0),
               "MXFP8 B 8192x8192 (MX)": snr(h["B4"], 2, o["q4b"], o["e4b"], 0),
               "MOSS X 16384x4096 (MOSS, E4M3)": snr(h["X5"], 3, o["q5X"], o["e5X"], 0, S5["X"]),
               "MOSS W 4096x4096 (MOSS, E4M3)": snr(h["W5"], 3, o["q5W"], o["e5W"], 0, S5["W"]),

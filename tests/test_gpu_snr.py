@@ -3,6 +3,9 @@ write: SNR_dB = 10 log10(sum x^2 / sum (x - x_hat)^2) in fp64 over the whole ten
 oracle's exact dequantization of the GPU's output (page "MOSS:高效、精确的 FP8 LLM 训练 ...",
 section 2, eq. 4, read as power ratio then decibels).
 
+  fine-grained:    X 4096 x 7168 (0.1% of entries x50) under its own 1x128 scaling and per-tensor
+                   current, beside the same X without the outliers; W 2048 x 7168 under 128x128
+                   blocks and per-tensor current;
   MXFP8 workload:  A and B 8192 x 8192 under MX, with per-tensor current and 1x128 for context;
   MOSS workload:   X, W (E4M3) and dY (E5M2) under MOSS, 1x128 and per-tensor current.
 
@@ -37,9 +40,10 @@ def _snr(fq, orc, bits, scheme, fmt):
     if scheme == "per-tensor":
         q, _, s, _ = fq.quantize(xd, TENSOR, fmt)
         xhat = orc.dequantize(TENSOR, host(q), fmt, None, np.float32(host(s)[0]))
-    elif scheme == "1x128":
-        q, s, _, _ = fq.quantize(xd, BLOCK, fmt, block=(1, 128))
-        xhat = orc.dequantize(BLOCK, host(q), fmt, host(s), None, block=(1, 128))
+    elif scheme in ("1x128", "128x128"):
+        blk = (1, 128) if scheme == "1x128" else (128, 128)
+        q, s, _, _ = fq.quantize(xd, BLOCK, fmt, block=blk)
+        xhat = orc.dequantize(BLOCK, host(q), fmt, host(s), None, block=blk)
     elif scheme == "MX":
         q, e, _, _ = fq.quantize(xd, MX, fmt)
         xhat = orc.dequantize(MX, host(q), fmt, host(e))
@@ -56,6 +60,26 @@ def _table(fq, orc, tensors, schemes):
         out[name] = {sc: _snr(fq, orc, bits, sc, fmt) for sc in schemes}
         print("SNR dB %-28s %s" % (name, "  ".join("%s %.3f" % kv for kv in out[name].items())))
     return out
+
+
+def test_snr_fine_grained_workload(fq, orc):
+    """The ×50 outliers (0.1% of X) barely move the per-tensor SNR of FP8 E4M3, whose relative
+    precision is the same across its normal range, but they widen the lead of 1x128 scaling: a
+    group that holds an outlier maps it to the format's maximum, where it is exact or nearly so,
+    and the outliers carry most of the tensor's power (0.001 x 2500 = 2.5 times the rest)."""
+    X, W = workloads.fine_grained_inputs()
+    Xc, _ = workloads.fine_grained_inputs(outlier_frac=0.0)
+    t = _table(fq, orc, {"fine-grained X 4096x7168": (X, E4M3), "same X, no outliers": (Xc, E4M3)},
+               ("1x128", "per-tensor"))
+    tw = _table(fq, orc, {"fine-grained W 2048x7168": (W, E4M3)}, ("128x128", "per-tensor"))
+    for name, r in t.items():
+        assert r["1x128"] >= r["per-tensor"], name
+    r = tw["fine-grained W 2048x7168"]
+    assert r["128x128"] >= r["per-tensor"] - 1e-3
+    lead = t["fine-grained X 4096x7168"]["1x128"] - t["fine-grained X 4096x7168"]["per-tensor"]
+    lead_clean = t["same X, no outliers"]["1x128"] - t["same X, no outliers"]["per-tensor"]
+    print("1x128 - per-tensor: %+.3f dB with the outliers, %+.3f dB without" % (lead, lead_clean))
+    assert lead > lead_clean
 
 
 def test_snr_mx_workload(fq, orc):
