@@ -346,10 +346,11 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def measure_casts_cold_warm(torch, fq, o, w2, w3, w4, w5, reps=10):
-    """Each cast of the step timed alone (HIP events around it), cold and warm.  Cold: before every
-    launch a 1 GiB buffer is read, which leaves only clean, unrelated lines in L2 and the 256 MB
-    last-level cache, so the input comes from HBM and no earlier writes are pending.  Warm: the
+def measure_casts_cold_warm(torch, fq, o, w2, w3, w4, w5, reps=20, warmup=5):
+    """Each cast of the step timed alone (HIP events around it), cold and warm: after `warmup`
+    untimed launches, the median of `reps` cold launches and the mean of `reps` warm ones.  Cold:
+    before every launch a 1 GiB buffer is read, which leaves only clean, unrelated lines in L2 and
+    the 256 MB last-level cache, so the input comes from HBM and no earlier writes are pending.  Warm: the
     same launch repeated back to back, so an input that fits the last-level cache is served from
     it.  GB/s counts the algorithmic bytes (input read, plus the amax pass's read where the scale
     is derived, FP8 and scale bytes written).  A plain device copy (256 MiB read, 256 MiB written,
@@ -378,7 +379,8 @@ def measure_casts_cold_warm(torch, fq, o, w2, w3, w4, w5, reps=10):
     casts["device copy 256 MiB (reference)"] = (lambda: torch.neg(csrc, out=cdst), 2 * csrc.numel() * 4)
     out = {}
     for name, (fn, nbytes) in casts.items():
-        fn()
+        for _ in range(warmup):
+            fn()
         torch.cuda.synchronize()
         cold = []
         for _ in range(reps):
