@@ -73,13 +73,39 @@ GEMM_SOURCES = ("fp8_scaled_quantization_amd/csrc/gemm_pp.cuh", "fp8_scaled_quan
                 "fp8_scaled_quantization_amd/csrc/common.cuh")
 
 
+def _code_only(text):
+    """C++ source with its comments removed and whitespace runs collapsed (string and character
+    literals kept), so that the digest below changes with the code, not with its comments."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def gemm_source_digest():
+    """SHA-256 over the GEMM sources' code (comments and layout excluded)."""
     import hashlib
     h = hashlib.sha256()
     root = os.path.dirname(os.path.abspath(__file__))
     for rel in GEMM_SOURCES:
-        with open(os.path.join(root, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(root, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 
