@@ -128,16 +128,21 @@ def edge_indices(n: int, tile: int = 128) -> np.ndarray:
 
 
 def check_gemm_large(orc, C32, Cbf, deqA, deqB, M: int, N: int, K: int, seed: int, label: str,
-                     promoted: bool = False, n_random: int = 65536, tile: int = 128) -> float:
-    """Full-size GEMM parity on three sets of outputs: every output of the rows on a tile edge
-    (first and last row of every `tile` rows), every output of the columns on a tile edge, and
-    n_random seeded outputs anywhere.  A 128-edge grid contains the edges of every kernel's tiles
-    (256 x 256, 256 x 128, 128 x 128).  C32 / Cbf are the device outputs (fp32 and bf16) of the
-    same problem; deqA / deqB dequantize a list of operand rows with the oracle."""
+                     promoted: bool = False, n_random: int = 65536, tile: int = 128, full: bool = False) -> float:
+    """Full-size GEMM parity.  With full=True every output is compared.  Otherwise three sets of
+    outputs: every output of the rows on a tile edge (first and last row of every `tile` rows),
+    every output of the columns on a tile edge, and n_random seeded outputs anywhere; a 128-edge
+    grid contains the edges of every kernel's tiles (256 x 256, 256 x 128, 128 x 128).  C32 / Cbf
+    are the device outputs (fp32 and bf16) of the same problem; deqA / deqB dequantize a list of
+    operand rows with the oracle."""
+    Aall, Ball = deqA(np.arange(M)), deqB(np.arange(N))
+    if full:
+        Cref, D, E, Sg = reference_terms(orc, Aall, Ball, promoted=promoted)
+        del Aall, Ball
+        return check_gemm(host(C32), host(Cbf), Cref, D, E, K, "%s, all %d outputs" % (label, M * N), Sg)
     er, ec = edge_indices(M, tile), edge_indices(N, tile)
     rng = np.random.default_rng(seed)
     pairs = np.stack([rng.integers(0, M, n_random), rng.integers(0, N, n_random)], 1).astype(np.int64)
-    Aall, Ball = deqA(np.arange(M)), deqB(np.arange(N))
     worst = 0.0
     rt = torch.from_numpy(er).to(C32.device)
     ct = torch.from_numpy(ec).to(C32.device)

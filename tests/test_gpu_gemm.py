@@ -1,8 +1,8 @@
 """GPU parity of the scaled FP8 GEMM against the oracle's fp64 product of the same quantized
 operands, with the elementwise bound derived in tests/gpu_util.py: full comparison on small and
-ragged shapes (several tiles and partial tiles), and at the five workloads' full shapes, in the
-launch configuration the benchmark times, every output on a 128-tile edge row or column plus
-65,536 seeded outputs anywhere (tests/gpu_util.check_gemm_large)."""
+ragged shapes (several tiles and partial tiles), and at the workloads' full shapes, in the launch
+configuration the benchmark times, every output of the fine-grained, MXFP8 and MOSS products
+(tests/gpu_util.check_gemm_large)."""
 import numpy as np
 import pytest
 import torch
@@ -130,10 +130,10 @@ def _rows_deq(orc, mode, hq, hs, hg, fmt, block):
     return f
 
 
-def _large_check(fq, orc, mode, A, afmt, B, bfmt, deqA, deqB, M, N, K, seed, label):
+def _large_check(fq, orc, mode, A, afmt, B, bfmt, deqA, deqB, M, N, K, seed, label, full=True):
     C32 = _run(fq, mode, A, afmt, B, bfmt, OUT_F32)
     Cbf = _run(fq, mode, A, afmt, B, bfmt, OUT_BF16)
-    return check_gemm_large(orc, C32, Cbf, deqA, deqB, M, N, K, seed, label, promoted=mode == BLOCK)
+    return check_gemm_large(orc, C32, Cbf, deqA, deqB, M, N, K, seed, label, promoted=mode == BLOCK, full=full)
 
 
 def test_gemm_fine_grained_full_size(fq, orc):
@@ -152,24 +152,33 @@ def test_gemm_mx_full_size(fq, orc):
                  _rows_deq(orc, MX, hqb, hsb, None, E4M3, None), 8192, 8192, 8192, 4, "mx 8192^3")
 
 
-def test_gemm_moss_forward_backward_full_size(fq, orc):
+@pytest.fixture(scope="module")
+def moss_operands(fq, orc):
+    """The MOSS workload's six quantized copies (device) with their host bytes and scales."""
     X, W, dY = workloads.moss_inputs()
-    Xq, (hx, hxs, hxg) = _quant_operand(fq, orc, X, MOSS, E4M3, None)
-    Wq, (hw, hws, hwg) = _quant_operand(fq, orc, W, MOSS, E4M3, None)
-    Gq, (hg_, hgs, hgg) = _quant_operand(fq, orc, dY, MOSS, E5M2, None)
-    XTq, (hxt, hxts, _) = _quant_operand(fq, orc, X, MOSS, E4M3, None, transpose=True, S=Xq[2])
-    WTq, (hwt, hwts, _) = _quant_operand(fq, orc, W, MOSS, E4M3, None, transpose=True, S=Wq[2])
-    GTq, (hgt, hgts, _) = _quant_operand(fq, orc, dY, MOSS, E5M2, None, transpose=True, S=Gq[2])
-    d = lambda hq, hs, hg, fmt: _rows_deq(orc, MOSS, hq, hs, hg, fmt, None)
-    # Y = X W^T
-    _large_check(fq, orc, MOSS, Xq, E4M3, Wq, E4M3, d(hx, hxs, hxg, E4M3), d(hw, hws, hwg, E4M3),
-                 16384, 4096, 4096, 51, "moss Y")
-    # dX = dY W  (B = W^T, grouped along out)
-    _large_check(fq, orc, MOSS, Gq, E5M2, WTq, E4M3, d(hg_, hgs, hgg, E5M2), d(hwt, hwts, hwg, E4M3),
-                 16384, 4096, 4096, 52, "moss dX")
-    # dW = dY^T X  (A = dY^T, B = X^T, grouped along tokens)
-    _large_check(fq, orc, MOSS, GTq, E5M2, XTq, E4M3, d(hgt, hgts, hgg, E5M2), d(hxt, hxts, hxg, E4M3),
-                 4096, 4096, 16384, 53, "moss dW")
+    o = {}
+    o["X"] = _quant_operand(fq, orc, X, MOSS, E4M3, None)
+    o["W"] = _quant_operand(fq, orc, W, MOSS, E4M3, None)
+    o["G"] = _quant_operand(fq, orc, dY, MOSS, E5M2, None)
+    o["XT"] = _quant_operand(fq, orc, X, MOSS, E4M3, None, transpose=True, S=o["X"][0][2])
+    o["WT"] = _quant_operand(fq, orc, W, MOSS, E4M3, None, transpose=True, S=o["W"][0][2])
+    o["GT"] = _quant_operand(fq, orc, dY, MOSS, E5M2, None, transpose=True, S=o["G"][0][2])
+    yield o
+    o.clear()
+    torch.cuda.empty_cache()
+
+
+# Y = X W^T; dX = dY W (B = W^T, grouped along out); dW = dY^T X (A = dY^T, B = X^T, grouped along
+# tokens).  Every output of each product at the workload's size.
+@pytest.mark.parametrize("gemm", ["Y", "dX", "dW"])
+def test_gemm_moss_forward_backward_full_size(fq, orc, moss_operands, gemm):
+    a, af, b, bf, M, N, K, seed = {"Y": ("X", E4M3, "W", E4M3, 16384, 4096, 4096, 51),
+                                   "dX": ("G", E5M2, "WT", E4M3, 16384, 4096, 4096, 52),
+                                   "dW": ("GT", E5M2, "XT", E4M3, 4096, 4096, 16384, 53)}[gemm]
+    # (the transposed copies were cast with the row-grouped copy's global scale, which they return)
+    (Aq, (ha, has_, hag)), (Bq, (hb, hbs, hbg)) = moss_operands[a], moss_operands[b]
+    _large_check(fq, orc, MOSS, Aq, af, Bq, bf, _rows_deq(orc, MOSS, ha, has_, hag, af, None),
+                 _rows_deq(orc, MOSS, hb, hbs, hbg, bf, None), M, N, K, seed, "moss " + gemm)
 
 
 # Shapes with enough 256 x 256 tiles (>= 192) to take the ping-pong kernel, with partial tiles in
