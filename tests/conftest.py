@@ -30,5 +30,11 @@ def pytest_collection_modifyitems(config, items):
 @pytest.fixture(scope="session")
 def orc():
     from oracle import oracle
+    src = os.environ.get("FP8Q_ORACLE_SOURCE")
+    if src:
+        # the oracle built from another source file: tests/test_oracle_mutants.py runs the oracle's
+        # pins against copies of oracle.c with one planted mistake each
+        oracle._SRC = src
+        oracle._LIB_PATH = os.path.splitext(src)[0] + ".so"
     oracle.lib()
     return oracle

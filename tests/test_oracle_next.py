@@ -215,6 +215,23 @@ def test_block_dequantize_fp32_scales_vs_numpy_and_torch(orc):
     assert np.array_equal(gotbf, wantbf)
 
 
+def test_block_dequantize_bf16_ties_to_even(orc):
+    """bf16 output of products that fall exactly halfway between two bf16 values: codes whose value
+    is a power of two times a scale of 1 + 2^-8 (the ninth significand bit, the first that bf16
+    drops) round to the even neighbour, as torch's fp32 -> bf16 conversion does; 1 + 3 * 2^-8 and
+    1.5 + 2^-8 give ties whose even neighbour is above."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)     # every finite E4M3 code
+    q = np.resize(codes, 128 * 384).reshape(128, 384)
+    s = np.array([[1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.5 + 2.0 ** -8]], np.float32)
+    dec = orc.decode_array(q, E4M3).astype(np.float32)
+    want32 = dec * np.repeat(s, 128, 1)                    # exact: at most 4 + 9 significand bits
+    ties = (want32.view(np.uint32) & 0xFFFF) == 0x8000
+    assert ties.sum() > 1000
+    got = orc.block_dequantize(BLOCK, q, E4M3, s, (128, 128), out_bf16=True)
+    want = torch.from_numpy(want32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+
+
 def test_block_dequantize_e8m0_is_exact(orc):
     W = workloads.random_matrix(13, 256, 256, 0.05)
     q, e8 = orc.quantize_block_e8m0(W, E4M3, 128, 128)
