@@ -68,6 +68,30 @@ MUTANTS = {
         "sig += fabs(prefix);\n        prefix += part;", "prefix += part;\n        sig += fabs(prefix);"),
     "SNR as 20 log10 of a power ratio": (
         "return 10.0 * log10(sig / noise);", "return 20.0 * log10(sig / noise);"),
+    "SNR noise as absolute differences": (
+        "noise += d * d;", "noise += fabs(d);"),
+    "E4M3 decodes every top-exponent code as NaN": (
+        "if (e == 15 && m == 7) return NAN;", "if (e == 15) return NAN;"),
+    "NaN encodes without its sign": (
+        "if (isnan(v)) return (uint8_t)(sign | 0x7F);", "if (isnan(v)) return (uint8_t)0x7F;"),
+    "scale of an infinite amax is not the fallback": (
+        "if (!(amax > 0.0f) || isinf(amax)) return fallback;", "if (!(amax > 0.0f)) return fallback;"),
+    "history inserts the newest amax at the end": (
+        "hist[0] = amax_new;", "hist[len - 1] = amax_new;"),
+    "automatic scaling keeps the sum at a rescale": (
+        "state[1] = 0.0f;", "state[1] = state[1];"),
+    "block dequantization swaps the block extents": (
+        "else if (mode == ORC_BLOCK) s = (double)((const float*)scales)[(r / br) * nbc + k / bc];",
+        "else if (mode == ORC_BLOCK) s = (double)((const float*)scales)[(r / bc) * nbc + k / br];"),
+    "UE8M0 dequantization negates the exponent": (
+        "s = ldexp(1.0, (int)((const uint8_t*)scales)[(r / br) * nbc + k / bc] - 127);",
+        "s = ldexp(1.0, 127 - (int)((const uint8_t*)scales)[(r / br) * nbc + k / bc]);"),
+    "MOSS global factor from the first row only": (
+        "float S = orc_compute_scale(orc_amax(x, in_kind, rows, cols, ld), fmt, 1.0f);",
+        "float S = orc_compute_scale(orc_amax(x, in_kind, 1, cols, ld), fmt, 1.0f);"),
+    "block fp32 scale fallback is zero": (
+        "float s = orc_compute_scale(amax_f32(t, C, r0, r1, c0, c1), fmt, 1.0f);",
+        "float s = orc_compute_scale(amax_f32(t, C, r0, r1, c0, c1), fmt, 0.0f);"),
 }
 
 
