@@ -142,6 +142,7 @@ def _same_gpu(*ts) -> None:
 
 # ------------------------------------------------------------------ the entry points
 def fp8_amax(x: torch.Tensor, amax_out: torch.Tensor, stream=None) -> None:
+    """amax_out[0] = max |x| over a 2-D fp32 or bf16 tensor (NaN if any element is NaN)."""
     _mat(x, "x", (torch.float32, torch.bfloat16))
     _f32(amax_out, "amax_out")
     _same_gpu(x, amax_out)
@@ -151,6 +152,10 @@ def fp8_amax(x: torch.Tensor, amax_out: torch.Tensor, stream=None) -> None:
 def fp8_quantize(mode: int, fmt: int, x: torch.Tensor, q: torch.Tensor, scales=None, tensor_scale=None,
                  scale_is_input: bool = False, amax_out=None, block=(1, 128), transpose_out: bool = False,
                  stream=None) -> None:
+    """Cast x (2-D fp32/bf16) to FP8 bytes q under `mode`, writing the scales the mode uses: `scales`
+    (BLOCK: fp32 per block; MX/MOSS/BLOCK_E8M0: E8M0 bytes) and, for TENSOR/MOSS, `tensor_scale`
+    (derived from the amax, or read when scale_is_input).  transpose_out casts x^T.  Shapes are
+    checked here (see scale_shape) before the call."""
     _mat(x, "x", (torch.float32, torch.bfloat16))
     R, Kc = (x.shape[1], x.shape[0]) if transpose_out else (x.shape[0], x.shape[1])
     _mat(q, "q", (torch.uint8,), (R, Kc))
@@ -175,6 +180,9 @@ def fp8_quantize(mode: int, fmt: int, x: torch.Tensor, q: torch.Tensor, scales=N
 
 def fp8_quantize_dual(mode: int, fmt: int, x: torch.Tensor, q: torch.Tensor, scales, qt: torch.Tensor, scales_t,
                       tensor_scale=None, scale_is_input: bool = False, amax_out=None, stream=None) -> None:
+    """Both quantized copies of x in one call: q (rows x cols) grouped along each row and qt
+    (cols x rows) grouped along each column, with their E8M0 scales (MX/MOSS) and one shared
+    tensor scale (TENSOR/MOSS)."""
     _need(mode in (TENSOR, MX, MOSS), "fp8_quantize_dual: mode must be TENSOR, MX or MOSS")
     _mat(x, "x", (torch.float32, torch.bfloat16))
     R, C = x.shape
@@ -199,6 +207,8 @@ def fp8_quantize_dual(mode: int, fmt: int, x: torch.Tensor, q: torch.Tensor, sca
 
 def fp8_history_update(history: torch.Tensor, amax_new: torch.Tensor, scale: torch.Tensor, fmt: int,
                        stream=None) -> None:
+    """Delayed scaling: roll amax_new into the history window (newest at index 0) and set `scale`
+    from the window's max for the next step (kept when that max is zero or non-finite)."""
     _f32(history, "history")
     _f32(amax_new, "amax_new")
     _f32(scale, "scale")
@@ -209,6 +219,9 @@ def fp8_history_update(history: torch.Tensor, amax_new: torch.Tensor, scale: tor
 
 def fp8_scaled_gemm(mode: int, A: torch.Tensor, afmt: int, Ascale, B: torch.Tensor, bfmt: int, Bscale,
                     Aglobal, Bglobal, C: torch.Tensor, out_dtype: int, stream=None) -> None:
+    """C = dequant(A) . dequant(B)^T for FP8 bytes A (M x K) and B (N x K) with the mode's scales
+    (Ascale/Bscale per group or block; Aglobal/Bglobal fp32 tensor factors for TENSOR and MOSS, or
+    a static activation scale as Aglobal for BLOCK without Ascale); C is fp32 or bf16 (out_dtype)."""
     _mat(A, "A", (torch.uint8,))
     M, K = A.shape
     _mat(B, "B", (torch.uint8,))
@@ -244,6 +257,8 @@ def fp8_scaled_gemm(mode: int, A: torch.Tensor, afmt: int, Ascale, B: torch.Tens
 
 def fp8_history_merge(hist_dst: torch.Tensor, hist_src: torch.Tensor, scale_dst: torch.Tensor, scale_src: torch.Tensor,
                       stream=None) -> None:
+    """Merge two updates of one delayed-scaling state: history and scale become their elementwise
+    max (NaN propagates)."""
     _f32(hist_dst, "hist_dst", 0)
     _f32(hist_src, "hist_src", 0)
     _need(hist_dst.numel() == hist_src.numel(), "histories differ in length")
@@ -256,6 +271,8 @@ def fp8_history_merge(hist_dst: torch.Tensor, hist_src: torch.Tensor, scale_dst:
 
 def fp8_auto_scale(state: torch.Tensor, rescale: bool, amax_now, lr: float, fmt: int, scale_out: torch.Tensor,
                    stream=None) -> None:
+    """One step of automatic weight scaling: scale_out from the last measured weight max plus the
+    learning rates since (state = [base, lr sum]); a rescale step takes amax_now as the new base."""
     _f32(state, "state", 2)
     _f32(scale_out, "scale_out")
     if rescale:
@@ -268,6 +285,8 @@ def fp8_auto_scale(state: torch.Tensor, rescale: bool, amax_now, lr: float, fmt:
 
 
 def fp8_scale_to_e8m0(s: torch.Tensor, e8m0: torch.Tensor, bad_count: torch.Tensor, stream=None) -> None:
+    """Exact conversion of power-of-two fp32 scales to UE8M0 bytes; anything else becomes 0xFF and is
+    counted in bad_count[0]."""
     _f32(s, "s", 0)
     _need(e8m0.dtype == torch.uint8 and e8m0.numel() == s.numel() and e8m0.is_contiguous(),
           "e8m0 must be contiguous uint8 with s's size")
@@ -278,6 +297,8 @@ def fp8_scale_to_e8m0(s: torch.Tensor, e8m0: torch.Tensor, bad_count: torch.Tens
 
 def fp8_block_dequantize(mode: int, fmt: int, q: torch.Tensor, scales: torch.Tensor, out: torch.Tensor,
                          block=(128, 128), stream=None) -> None:
+    """out = decode(q) * block scale, one fp32 product per element, stored as fp32 or bf16 (RNE) by
+    out's dtype; scales are fp32 (BLOCK) or UE8M0 bytes (BLOCK_E8M0)."""
     _need(mode in (BLOCK, BLOCK_E8M0), "mode must be BLOCK or BLOCK_E8M0")
     _need(len(block) == 2 and int(block[0]) > 0 and int(block[1]) > 0,
           "block must be two positive integers, got %s" % (block,))
@@ -293,6 +314,8 @@ def fp8_block_dequantize(mode: int, fmt: int, q: torch.Tensor, scales: torch.Ten
 
 # ------------------------------------------------------------------ allocating conveniences
 def scale_shape(mode: int, out_rows: int, out_cols: int, block=(1, 128)):
+    """(shape, dtype) of the scale array fp8_quantize writes for an out_rows x out_cols output, or
+    (None, None) when the mode has none."""
     if mode == BLOCK:
         return (-(-out_rows // block[0]), -(-out_cols // block[1])), torch.float32
     if mode == BLOCK_E8M0:
