@@ -24,8 +24,8 @@ EXPORTS = ("fp8q_init", "fp8q_last_error", "fp8_amax", "fp8_quantize", "fp8_quan
            "fp8_scaled_gemm", "fp8_history_merge", "fp8_auto_scale", "fp8_scale_to_e8m0", "fp8_block_dequantize")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError("libfp8q.so is not built (run __graft_entry__.build() or "
-                      "python fp8_scaled_quantization_amd/build.py); there is no fallback path")
+    raise ImportError("libfp8q.so is not built (run python fp8_scaled_quantization_amd/build.py); "
+                      "there is no fallback path")
 
 _L = ctypes.CDLL(LIB_PATH)
 _P, _I64, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
