@@ -117,6 +117,18 @@ __device__ __forceinline__ v8i frag(const uint8_t* row, uint32_t lo, uint32_t hi
     return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
 
+// Byte g of each of four scale words w0..w3, packed as bytes 0..3 of one register.  v_perm_b32
+// takes bytes 0-3 from its second operand and 4-7 from its first, and a selector byte 0x0C gives
+// zero, so with sel = perm_selector(g) one permute puts byte g of w0 and of w1 in bytes 0 and 1;
+// two permutes and a shift-or give the register (one selector register, as many as a shift count).
+__device__ __forceinline__ uint32_t perm_selector(int g) {
+    return (uint32_t)g | ((uint32_t)(4 + g) << 8) | 0x0C0C0000u;
+}
+__device__ __forceinline__ uint32_t pack_scale_bytes(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
+                                                     uint32_t sel) {
+    return __builtin_amdgcn_perm(w1, w0, sel) | (__builtin_amdgcn_perm(w3, w2, sel) << 16);
+}
+
 // Block-scaled MFMA whose E8M0 scales sit in byte selA of sa and byte selB of sb (the byte
 // selects must be literals; callers pass loop indices of fully unrolled loops, so the switch folds).
 template <int AF, int BF>
@@ -399,17 +411,10 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
             if (SCALED) {
                 // byte g4 of a row's word = the E8M0 scale of (row, group g4) for this step; four
                 // subtiles per register, picked in the MFMA by its byte select
-                const int sh = 8 * g4;
-                uint32_t pa = 0, pb0 = 0, pb1 = 0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) pa |= ((sw[i] >> sh) & 0xFFu) << (8 * i);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) pb0 |= ((sw[4 + j] >> sh) & 0xFFu) << (8 * j);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) pb1 |= ((sw[8 + j] >> sh) & 0xFFu) << (8 * j);
-                sca = (int)pa;
-                scb0 = (int)pb0;
-                scb1 = (int)pb1;
+                const uint32_t sel = perm_selector(g4);
+                sca = (int)pack_scale_bytes(sw[0], sw[1], sw[2], sw[3], sel);
+                scb0 = (int)pack_scale_bytes(sw[4], sw[5], sw[6], sw[7], sel);
+                scb1 = (int)pack_scale_bytes(sw[8], sw[9], sw[10], sw[11], sel);
                 // finish the packing here, in the memory phase, not after the barrier
                 asm volatile("" ::"v"(sca), "v"(scb0), "v"(scb1));
             }

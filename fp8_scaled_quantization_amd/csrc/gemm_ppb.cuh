@@ -242,14 +242,9 @@ __global__ __launch_bounds__(512, 1) void gemm_ppb_kernel(GemmArgs g) {
         // MX/MOSS: four row blocks' scales per register, picked in the MFMA by its byte select
         int sca = 0, scb = 0;
         if (SCALED) {
-            const int sh = 8 * g4;
-            uint32_t pa = 0, pb = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pa |= ((swa[i] >> sh) & 0xFFu) << (8 * i);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) pb |= ((swb[j] >> sh) & 0xFFu) << (8 * j);
-            sca = (int)pa;
-            scb = (int)pb;
+            const uint32_t sel = pp::perm_selector(g4);
+            sca = (int)pp::pack_scale_bytes(swa[0], swa[1], swa[2], swa[3], sel);
+            scb = (int)pp::pack_scale_bytes(swb[0], swb[1], swb[2], swb[3], sel);
             asm volatile("" ::"v"(sca), "v"(scb));
         }
         // this wave's copies of step k+1 (sent one memory phase ago) land before the barrier; the

@@ -241,17 +241,10 @@ __global__ __launch_bounds__(512, 1) void gemm_pps_kernel(GemmArgs g) {
                 }
             }
             if (SCALED) {
-                const int sh = 8 * g4;
-                uint32_t pa = 0, pb0 = 0, pb1 = 0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) pa |= ((sw[i] >> sh) & 0xFFu) << (8 * i);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) pb0 |= ((sw[4 + j] >> sh) & 0xFFu) << (8 * j);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) pb1 |= ((sw[8 + j] >> sh) & 0xFFu) << (8 * j);
-                sca = (int)pa;
-                scb0 = (int)pb0;
-                scb1 = (int)pb1;
+                const uint32_t sel = pp::perm_selector(g4);
+                sca = (int)pp::pack_scale_bytes(sw[0], sw[1], sw[2], sw[3], sel);
+                scb0 = (int)pp::pack_scale_bytes(sw[4], sw[5], sw[6], sw[7], sel);
+                scb1 = (int)pp::pack_scale_bytes(sw[8], sw[9], sw[10], sw[11], sel);
                 asm volatile("" ::"v"(sca), "v"(scb0), "v"(scb1));
             }
             wait_lgkm0();
