@@ -92,6 +92,49 @@ MUTANTS = {
     "block fp32 scale fallback is zero": (
         "float s = orc_compute_scale(amax_f32(t, C, r0, r1, c0, c1), fmt, 1.0f);",
         "float s = orc_compute_scale(amax_f32(t, C, r0, r1, c0, c1), fmt, 0.0f);"),
+    "transposed operand left untransposed": (
+        "if (transpose) t[c * C + r] = v; else t[r * C + c] = v;",
+        "if (transpose) t[r * R + c] = v; else t[r * C + c] = v;"),
+    "bf16 input widened from the wrong bit position": (
+        "uint32_t b = (uint32_t)((const uint16_t*)x)[idx] << 16;",
+        "uint32_t b = (uint32_t)((const uint16_t*)x)[idx] << 15;"),
+    "overflow becomes NaN instead of saturating": (
+        "if (v > M) return M;",
+        "if (v > M) return NAN;"),
+    "negative overflow saturates to +MAX": (
+        "if (v < -M) return -M;",
+        "if (v < -M) return M;"),
+    "MX group exponent from the whole row's amax": (
+        "float am = amax_f32(t, C, r, r + 1, c0, c1);\n"
+        "            int e = smallest_pow2_exponent(orc_fp8_max(fmt), (double)am, -127, 127);\n"
+        "            e8m0[r * ng + g]",
+        "float am = amax_f32(t, C, r, r + 1, 0, C);\n"
+        "            int e = smallest_pow2_exponent(orc_fp8_max(fmt), (double)am, -127, 127);\n"
+        "            e8m0[r * ng + g]"),
+    "delayed step quantizes with the previous step's scale": (
+        "orc_quantize_tensor(x, in_kind, rows, cols, ld, fmt, s, transpose, q, ldq);",
+        "orc_quantize_tensor(x, in_kind, rows, cols, ld, fmt, *scale, transpose, q, ldq);"),
+    "history merge keeps the destination's scale": (
+        "*scale_dst = max_nan(*scale_dst, scale_src);",
+        "*scale_dst = max_nan(*scale_dst, *scale_dst);"),
+    "automatic scaling keeps the old base at a rescale": (
+        "state[0] = amax_now;",
+        "state[0] = state[0] > amax_now ? state[0] : amax_now;"),
+    "fp32 -> UE8M0 conversion accepts any significand": (
+        "if (m == 0.5 && ex - 1 >= -127 && ex - 1 <= 127) {",
+        "if (ex - 1 >= -127 && ex - 1 <= 127) {"),
+    "MX dequantization reads the scales column-major": (
+        "s = ldexp(1.0, (int)((const uint8_t*)scales)[r * ng + k / 32] - 127);",
+        "s = ldexp(1.0, (int)((const uint8_t*)scales)[(k / 32) * rows + r] - 127);"),
+    "MOSS elements scaled by 2^e instead of 2^-e": (
+        "float f = (float)ldexp(1.0, -e);\n            for (int64_t c = c0; c < c1; ++c) {\n"
+        "                float v = (t[r * C + c] / S) * f;",
+        "float f = (float)ldexp(1.0, e);\n            for (int64_t c = c0; c < c1; ++c) {\n"
+        "                float v = (t[r * C + c] / S) * f;"),
+    "tensor amax ignores NaN": (
+        "    return nan_seen ? NAN : m;\n}\n\n/* ----------------------------------------------------------------"
+        " scales",
+        "    return m;\n}\n\n/* ---------------------------------------------------------------- scales"),
 }
 
 

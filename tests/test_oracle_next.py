@@ -127,6 +127,22 @@ def test_auto_scale_is_tight_on_the_worst_case_trajectory(orc):
         w[1, 3] += lr                              # the optimizer step after the forward pass
 
 
+def test_auto_scale_rescale_restarts_from_a_smaller_max(orc):
+    """A rescale takes the fresh max-reduction as the new base even when the weights have shrunk
+    (decay, clipping): the step's scale is then exactly the just-in-time scale of the smaller max,
+    not the larger prediction carried over from the previous interval."""
+    lr = np.float32(2.0 ** -12)
+    state = np.zeros(2, np.float32)
+    w = np.zeros((4, 8), np.float32)
+    w[2, 5] = 1.0
+    for t in range(10):
+        orc.auto_scale_step(state, t == 0, orc.amax(w) if t == 0 else 0.0, lr, E4M3)
+    w[2, 5] = 0.25                                 # the weights shrank before the next interval
+    s = orc.auto_scale_step(state, True, orc.amax(w), lr, E4M3)
+    assert s == _jit_scale(orc, w, E4M3) == np.float32(0.25) / np.float32(448.0)
+    assert state[0] == np.float32(0.25) and state[1] == lr
+
+
 def test_auto_scale_zero_weight_falls_back(orc):
     state = np.zeros(2, np.float32)
     assert orc.auto_scale_step(state, True, 0.0, 0.0, E4M3) == 1.0
