@@ -28,6 +28,10 @@ int check_launch(const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+// at most kSmallCastElems elements, tested without forming a product that could overflow
+bool small_tensor(int64_t rows, int64_t cols) {
+    return rows <= fp8q::kSmallCastElems && cols <= fp8q::kSmallCastElems && rows * cols <= fp8q::kSmallCastElems;
+}
 
 // Per-device result of the architecture check (up to 64 devices).
 int g_arch_ok[64];   // 0 unknown, 1 gfx950, -1 other
@@ -74,7 +78,7 @@ int fp8_amax(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld
     if (!valid_in(in_dtype)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_amax: in_dtype %d is not FP8Q_IN_F32/BF16", in_dtype);
     if (rows < 0 || cols < 0 || ld < cols) return fail(FP8Q_ERR_INVALID_ARG, "fp8_amax: bad shape rows=%lld cols=%lld ld=%lld",
                                                       (long long)rows, (long long)cols, (long long)ld);
-    if (!amax_out || (!x && rows * cols > 0)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_amax: NULL pointer");
+    if (!amax_out || (!x && rows > 0 && cols > 0)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_amax: NULL pointer");
     if (cols % 8 || ld % 8 || !aligned16(x)) return fail(FP8Q_ERR_UNSUPPORTED, "fp8_amax: cols and ld must be multiples of 8 and x 16-byte aligned");
     int rc = check_device();
     if (rc) return rc;
@@ -96,7 +100,7 @@ int fp8_quantize(int mode, int fmt, const void* x, int in_dtype, int64_t rows, i
     const int64_t R = transpose_out ? cols : rows, K = transpose_out ? rows : cols;
     if (ldq < K) return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: ldq=%lld is smaller than the output row length %lld",
                              (long long)ldq, (long long)K);
-    const bool empty = rows * cols == 0;
+    const bool empty = rows == 0 || cols == 0;
     if (!empty && (!x || !q)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: NULL x or q");
     if ((mode == FP8Q_BLOCK || mode == FP8Q_BLOCK_E8M0) && (block_r <= 0 || block_c <= 0))
         return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize: block size (%d, %d) must be two positive integers", block_r, block_c);
@@ -131,7 +135,7 @@ int fp8_quantize(int mode, int fmt, const void* x, int in_dtype, int64_t rows, i
     a.block_r = block_r;
     a.block_c = block_c;
     a.vec_out = ldq % 16 == 0 && aligned16(q);
-    if (mode == FP8Q_TENSOR && needs_amax && !empty && rows * cols <= fp8q::kSmallCastElems) {
+    if (mode == FP8Q_TENSOR && needs_amax && !empty && small_tensor(rows, cols)) {
         // small tensor: amax, scale and cast in one launch
         a.amax_out = amax_out;
         a.scale_out = tensor_scale;
@@ -173,7 +177,7 @@ int fp8_quantize_dual(int mode, int fmt, const void* x, int in_dtype, int64_t ro
     if (ldq < cols || ldqt < rows)
         return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize_dual: ldq=%lld / ldqt=%lld smaller than cols=%lld / rows=%lld",
                     (long long)ldq, (long long)ldqt, (long long)cols, (long long)rows);
-    const bool empty = rows * cols == 0;
+    const bool empty = rows == 0 || cols == 0;
     if (!empty && (!x || !q || !qt)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize_dual: NULL x, q or qt");
     if (mode != FP8Q_TENSOR && !empty && (!scales || !scales_t))
         return fail(FP8Q_ERR_INVALID_ARG, "fp8_quantize_dual: NULL scales or scales_t");
@@ -219,7 +223,7 @@ int fp8_quantize_dual(int mode, int fmt, const void* x, int in_dtype, int64_t ro
     a.ldq2 = ldq;
     a.scales2 = scales;
     a.vec_out = true;
-    if (mode == FP8Q_TENSOR && needs_amax && !empty && rows * cols <= fp8q::kSmallCastElems) {
+    if (mode == FP8Q_TENSOR && needs_amax && !empty && small_tensor(rows, cols)) {
         // small tensor: amax, scale and both copies in one launch
         a.amax_out = amax_out;
         a.scale_out = tensor_scale;
@@ -265,13 +269,13 @@ int fp8_scaled_gemm(int mode, const uint8_t* A, int afmt, const void* Ascale, co
     if (M < 0 || N < 0 || K < 0 || lda < K || ldb < K || ldc < N)
         return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: bad shape M=%lld N=%lld K=%lld lda=%lld ldb=%lld ldc=%lld",
                     (long long)M, (long long)N, (long long)K, (long long)lda, (long long)ldb, (long long)ldc);
-    if (M * N > 0 && !C) return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: NULL C");
-    if (M * N * K > 0 && (!A || !B)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: NULL A or B");
+    if (M > 0 && N > 0 && !C) return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: NULL C");
+    if (M > 0 && N > 0 && K > 0 && (!A || !B)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: NULL A or B");
     if ((mode == FP8Q_TENSOR || mode == FP8Q_MOSS) && (!Aglobal || !Bglobal))
         return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: Aglobal and Bglobal are required for TENSOR and MOSS");
     const bool blocked = mode == FP8Q_BLOCK || mode == FP8Q_BLOCK_E8M0;
     const bool a_static = blocked && !Ascale && Aglobal;     // static per-tensor activation scale
-    if (mode != FP8Q_TENSOR && K > 0 && M * N > 0 && ((!Ascale && !a_static) || !Bscale))
+    if (mode != FP8Q_TENSOR && K > 0 && M > 0 && N > 0 && ((!Ascale && !a_static) || !Bscale))
         return fail(FP8Q_ERR_INVALID_ARG, "fp8_scaled_gemm: Ascale (or, for BLOCK, a static Aglobal) and Bscale are "
                     "required for BLOCK, BLOCK_E8M0, MX and MOSS");
     if (K > 0 && (K % 16 || lda % 16 || ldb % 16 || !aligned16(A) || !aligned16(B)))
@@ -355,7 +359,7 @@ int fp8_block_dequantize(int mode, int fmt, const uint8_t* q, int64_t rows, int6
     if (rows < 0 || cols < 0 || ldq < cols || ldo < cols)
         return fail(FP8Q_ERR_INVALID_ARG, "fp8_block_dequantize: bad shape rows=%lld cols=%lld ldq=%lld ldo=%lld",
                     (long long)rows, (long long)cols, (long long)ldq, (long long)ldo);
-    if (rows * cols > 0 && (!q || !scales || !out)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_block_dequantize: NULL pointer");
+    if (rows > 0 && cols > 0 && (!q || !scales || !out)) return fail(FP8Q_ERR_INVALID_ARG, "fp8_block_dequantize: NULL pointer");
     int rc = check_device();
     if (rc) return rc;
     fp8q::DequantArgs a{};

@@ -85,3 +85,21 @@ def test_next_entry_points_reject_bad_arguments(L):
     assert bd(1, 0, dummy, 128, 128, 128, dummy, 0, 128, dummy, 1, 128, None) == L.ERR_INVALID_ARG
     assert bd(1, 0, dummy, 128, 128, 128, dummy, 128, 128, dummy, 5, 128, None) == L.ERR_INVALID_ARG
     assert bd(4, 0, dummy, 128, 128, 64, dummy, 128, 128, dummy, 1, 128, None) == L.ERR_INVALID_ARG
+
+
+def test_null_pointers_rejected_at_extents_whose_product_overflows(L):
+    """Extents of 2^32 x 2^32 multiply to 2^64, which wraps to 0 in 64-bit arithmetic: the NULL
+    checks compare each extent with zero, so such a call is still rejected as invalid."""
+    lib = L.lib()
+    dummy = ctypes.c_void_p(16)
+    big = 1 << 32
+    g = lib.fp8_scaled_gemm
+    assert g(0, dummy, 0, None, dummy, 0, None, dummy, dummy, big, big, 32, 32, 32, None, 0, big, None) == L.ERR_INVALID_ARG
+    assert "NULL C" in _err(L)
+    assert g(0, None, 0, None, None, 0, None, dummy, dummy, big, big, 32, 32, 32, dummy, 0, big, None) == L.ERR_INVALID_ARG
+    assert "NULL A or B" in _err(L)
+    assert lib.fp8_amax(None, 1, big, big, big, dummy, None) == L.ERR_INVALID_ARG
+    assert lib.fp8_quantize(0, 0, None, 1, big, big, big, 1, 128, 0, None, big, None, dummy, 1, None, None) == L.ERR_INVALID_ARG
+    assert "NULL x or q" in _err(L)
+    bd = lib.fp8_block_dequantize
+    assert bd(1, 0, None, big, big, big, None, 128, 128, None, 1, big, None) == L.ERR_INVALID_ARG
